@@ -1,0 +1,316 @@
+"""Benchmark of the verify + commit hot path on one MI355X.
+
+One step = one MTP decode step of the workload: gdn_verify for every layer
+(captured once in a HIP graph and replayed, as the layer launches run inside a
+captured decode graph) followed by one gdn_commit_all_layers launch (outside
+the graph, as the commit runs after sampling). Inputs are seeded synthetic
+tensors already resident in HBM. The commit works in place, so each step
+starts from the previous step's committed state; its cost does not depend on
+the values.
+
+Prints one JSON line: state-updates/s (one update = one token applied to one
+128x128 head; verify counts every window token, commit every accepted token),
+per-kernel times from HIP events on the launch stream, the commit kernel's
+roofline against the 8 TB/s HBM peak, the native snapshot-every-token baseline
+timed the same way, and the CPU oracle timed on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_deltanet_speculative_gdn_amd as G  # noqa: E402
+from gated_deltanet_speculative_gdn_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+REC_TOKEN_BYTES = (128 + 128 + 1) * 4           # correction, key, gate (fp32)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "commit_counters.json")
+KERNEL_SOURCES = ["gated_deltanet_speculative_gdn_amd/csrc/gdn_commit.hip",
+                  "gated_deltanet_speculative_gdn_amd/csrc/gdn_device.hpp",
+                  "gated_deltanet_speculative_gdn_amd/csrc/gdn_kernels.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def i32(x):
+    return torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device="cuda")
+
+
+class Step:
+    """Device buffers and launch closures for one workload."""
+
+    def __init__(self, wl):
+        s = wl.spec
+        self.wl, self.s = wl, s
+        self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens)
+        self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens)
+        self.out = torch.zeros((s.layers, wl.tokens, s.hv, s.dv), device="cuda")
+        self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.slot = i32(wl.state_slot)
+        self.rec_slot = i32(wl.rec_slot)
+        self.tok = i32(wl.tok_start)
+        self.win = i32(wl.win_len)
+        self.n = i32(wl.n_accept)
+        self.snaps = None
+
+    def verify_all(self):
+        wl = self.wl
+        for layer in range(self.s.layers):
+            G.gdn_verify(self.pools, layer, self.slot, self.rec_slot, self.tok, self.win, None,
+                         wl.q(layer), wl.k(layer), wl.v(layer), wl.a[layer], wl.beta[layer],
+                         self.out[layer], err_flags=self.err)
+
+    def commit(self):
+        G.gdn_commit_all_layers(self.pools, self.slot, self.slot, self.rec_slot, self.n,
+                                err_flags=self.err)
+
+    def native_all(self):
+        wl, s = self.wl, self.s
+        if self.snaps is None:
+            self.snaps = [torch.empty((s.rows, s.hv, s.rec_tokens, 128, 128),
+                                      dtype=wl.state_dtype, device="cuda")
+                          for _ in range(s.layers)]
+        for layer in range(s.layers):
+            G.gdn_native_window(self.pools, layer, self.slot, self.tok, self.win, wl.q(layer),
+                                wl.k(layer), wl.v(layer), wl.a[layer], wl.beta[layer],
+                                self.out[layer], self.snaps[layer], err_flags=self.err)
+
+    def native_accept(self):
+        G.gdn_native_accept(self.pools, self.snaps, self.slot, self.n, err_flags=self.err)
+
+
+def accounting(wl):
+    """Update counts and algorithmic HBM bytes of one step."""
+    s = wl.spec
+    sb = 128 * 128 * (4 if wl.state_dtype == torch.float32 else 2)
+    real = (wl.state_slot >= 0) & (wl.win_len > 0)
+    w = wl.win_len[real].astype(np.int64)
+    n = wl.n_accept[real].astype(np.int64)
+    verify_updates = int(s.layers * s.hv * w.sum())
+    commit_updates = int(s.layers * s.hv * n.sum())
+    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * 4 + REC_TOKEN_BYTES)
+    verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok)
+    commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * REC_TOKEN_BYTES))
+    native_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * (per_tok - s.hv * REC_TOKEN_BYTES)
+                             + w.sum() * s.hv * sb)
+    accept_bytes = int(s.layers * s.hv * (n > 0).sum() * 2 * sb)
+    return dict(verify_updates=verify_updates, commit_updates=commit_updates,
+                verify_bytes_per_launch=verify_bytes_layer, commit_bytes_per_launch=commit_bytes,
+                native_bytes_per_launch=native_bytes_layer, accept_bytes_per_launch=accept_bytes)
+
+
+def timed_loop(steps, graph_fn, eager_fn, graph_launches):
+    """Run `steps` steps of graph replay + one eager launch; return wall ms per
+    step and the mean per-launch event times of both parts."""
+    sync = torch.cuda.synchronize
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    sync()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        graph_fn()
+        e1.record()
+        eager_fn()
+        e2.record()
+    sync()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    g_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    c_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    return wall, g_ms / graph_launches, c_ms, g_ms
+
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def cpu_baseline(wl, acc):
+    """The oracle (plain C, OpenMP over heads) on one full step of the same
+    workload: every layer's real rows, windows and accepted counts."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import oracle_pool as OP
+    s = wl.spec
+    real = np.nonzero((wl.state_slot >= 0) & (wl.win_len > 0))[0]
+    nthreads = oracle.default_threads()
+    spent = 0.0
+    for layer in range(s.layers):
+        g = OP.gather(wl, layer, real)
+        keep = np.repeat(wl.n_accept[real], s.hv)[:, None]
+        t0 = time.perf_counter()
+        oracle.native_heads(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
+                            keep=keep, nthreads=nthreads)
+        spent += time.perf_counter() - t0
+    updates = acc["verify_updates"] + acc["commit_updates"]
+    return {"value": updates / spent, "unit": "state-updates/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(spent, 3),
+            "sample": f"one full step of {s.name}: {s.layers} layers x {len(real)} rows x "
+                      f"{s.hv} heads, native per-token rule with the accepted state kept"}
+
+
+def counters_traffic(commit_launch_bytes):
+    """HBM bytes per commit launch from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != source_hash() or not c.get("bytes_per_launch"):
+        return None
+    return int(c["bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.MTP_B64.name, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--no-native", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also time a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
+              "needs no collective and shards by heads, rows or layers)", file=sys.stderr)
+        sys.exit(2)
+    spec = W.WORKLOADS[args.workload]
+    if spec.ring_steps:
+        print("the ring workload is a parity case; bench the MTP workloads", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    G.load_library()
+    dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
+    log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    acc = accounting(wl)
+    st = Step(wl)
+    L = spec.layers
+
+    # warm-up (also loads the code object before capture)
+    for _ in range(max(args.warmup, 1)):
+        st.verify_all()
+        st.commit()
+    torch.cuda.synchronize()
+    graph = capture(st.verify_all)
+    for _ in range(args.warmup):
+        graph.replay()
+        st.commit()
+    torch.cuda.synchronize()
+    wall, ver_ms, com_ms, graph_ms = timed_loop(args.steps, graph.replay, st.commit, L)
+    assert st.err.item() == 0, f"device row errors {st.err.item()}"
+    log(f"step {wall:.3f} ms: verify graph {graph_ms:.3f} ms ({ver_ms * 1e3:.1f} us/layer), "
+        f"commit {com_ms * 1e3:.1f} us")
+
+    updates = acc["verify_updates"] + acc["commit_updates"]
+    value = updates / (wall / 1e3)
+    com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
+    ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
+    step_gbs = (L * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
+    traffic = counters_traffic(acc["commit_bytes_per_launch"])
+
+    result = {
+        "metric": "commit+verify state-updates/s and achieved HBM GB/s (% peak), B=64 D=4 48 layers",
+        "value": value,
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "layers": L, "batch": spec.rows,
+                   "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
+                   "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
+                   "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
+        "roofline": {"bound": "hbm", "kernel": "commit_all_layers",
+                     "achieved": com_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": com_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "kernels": {
+            "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": L,
+                       "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
+                       "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
+            "commit_all_layers": {"us_per_launch": com_ms * 1e3, "launches_per_step": 1,
+                                  "algorithmic_bytes_per_launch": acc["commit_bytes_per_launch"],
+                                  "GB/s": com_gbs, "frac_of_peak": com_gbs / HBM_PEAK_GBS},
+        },
+        "step_GB/s": step_gbs,
+        "updates_per_step": {"verify": acc["verify_updates"], "commit": acc["commit_updates"]},
+        "kernel_source_hash": source_hash(),
+    }
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        a = torch.empty(nbytes // 4, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        result["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes,
+                                "us": ms * 1e3, "GB/s": 2 * nbytes / (ms / 1e3) / 1e9}
+        del a, b
+
+    if not args.no_native:
+        native_graph = capture(st.native_all)
+        for _ in range(args.warmup):
+            native_graph.replay()
+            st.native_accept()
+        torch.cuda.synchronize()
+        nwall, nv_ms, na_ms, _ = timed_loop(args.steps, native_graph.replay, st.native_accept, L)
+        result["native_baseline"] = {
+            "what": "same verify arithmetic writing the state after every draft token, "
+                    "then one all-layer copy of the accepted state",
+            "ms_per_step": nwall, "value": updates / (nwall / 1e3), "unit": "state-updates/s",
+            "window_us_per_launch": nv_ms * 1e3,
+            "window_GB/s": acc["native_bytes_per_launch"] / (nv_ms / 1e3) / 1e9,
+            "accept_us": na_ms * 1e3,
+            "accept_GB/s": acc["accept_bytes_per_launch"] / (na_ms / 1e3) / 1e9,
+            "speedup_of_replay": nwall / wall,
+        }
+        log(f"native: step {nwall:.3f} ms (window {nv_ms * 1e3:.1f} us/layer, accept {na_ms * 1e3:.1f} us)")
+        st.snaps = None
+        del native_graph
+
+    if not args.no_cpu:
+        log("timing the CPU oracle on one full step ...")
+        result["cpu_baseline"] = cpu_baseline(wl, acc)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) verify-and-commit replay for Gated DeltaNet recurrent state.
+
+The hot path is hand-written HIP in ``csrc/`` behind the C ABI of
+``include/gdn_replay.h``; this package holds the ctypes binding (argument
+marshalling only), the in-tree build script and the seeded workload
+generators.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, GDN_MAX_LAYERS, GDN_MAX_REC_TOKENS, GdnError, Pools, ROW_BND, ROW_N, ROW_POS,
+    ROW_REC, ROW_SLOT, ROW_TABLE, ROW_WIN, gdn_align_plan, gdn_commit_all_layers,
+    gdn_native_accept, gdn_native_window, gdn_verify, load_library, rec_stride,
+)

@@ -1,0 +1,233 @@
+"""ctypes binding of ``libgdnreplay.so`` (the C ABI in include/gdn_replay.h).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+element strides and the current HIP stream, and every call goes straight to
+the library's entry point of the same name. No arithmetic of the method runs
+here, and there is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+GDN_MAX_LAYERS = 64
+GDN_HEAD_DIM = 128
+GDN_MAX_REC_TOKENS = 32
+GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
+ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
+
+EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_align_plan", "gdn_native_window",
+           "gdn_native_accept", "gdn_rec_stride", "gdn_status_string", "gdn_abi_version")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class gdn_pools(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32), ("num_v_heads", C.c_int32), ("num_k_heads", C.c_int32),
+        ("head_k_dim", C.c_int32), ("head_v_dim", C.c_int32), ("state_dtype", C.c_int32),
+        ("num_state_slots", C.c_int32), ("num_rec_slots", C.c_int32),
+        ("rec_tokens", C.c_int32), ("reserved", C.c_int32),
+        ("state", C.c_void_p * GDN_MAX_LAYERS), ("rec", C.c_void_p * GDN_MAX_LAYERS),
+    ]
+
+
+class gdn_verify_io(C.Structure):
+    _fields_ = [
+        ("q", C.c_void_p), ("q_tok_stride", C.c_int64), ("q_head_stride", C.c_int64),
+        ("k", C.c_void_p), ("k_tok_stride", C.c_int64), ("k_head_stride", C.c_int64),
+        ("v", C.c_void_p), ("v_tok_stride", C.c_int64), ("v_head_stride", C.c_int64),
+        ("a_log", C.c_void_p), ("beta", C.c_void_p), ("gate_tok_stride", C.c_int64),
+        ("out", C.c_void_p), ("out_tok_stride", C.c_int64), ("out_head_stride", C.c_int64),
+        ("num_tokens", C.c_int64), ("scale", C.c_float), ("reserved", C.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> C.CDLL:
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = C.CDLL(path)
+    P = C.POINTER
+    vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    lib.gdn_verify.argtypes = [P(gdn_pools), i32, i32, vp, vp, vp, vp, vp, P(gdn_verify_io), vp, vp]
+    lib.gdn_commit_all_layers.argtypes = [P(gdn_pools), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_align_plan.argtypes = [i32, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.gdn_native_window.argtypes = [P(gdn_pools), i32, i32, vp, vp, vp, P(gdn_verify_io), vp,
+                                      vp, vp]
+    lib.gdn_native_accept.argtypes = [P(gdn_pools), P(vp), i32, vp, vp, vp, vp]
+    for name in ("gdn_verify", "gdn_commit_all_layers", "gdn_align_plan", "gdn_native_window",
+                 "gdn_native_accept", "gdn_abi_version"):
+        getattr(lib, name).restype = C.c_int32
+    lib.gdn_rec_stride.argtypes = [i32]
+    lib.gdn_rec_stride.restype = C.c_int64
+    lib.gdn_status_string.argtypes = [i32]
+    lib.gdn_status_string.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> int:
+    if status != 0:
+        raise GdnError(status, load_library().gdn_status_string(status).decode())
+    return status
+
+
+def rec_stride(rec_tokens: int) -> int:
+    """Floats per (record slot, value head) block, from the library."""
+    return int(load_library().gdn_rec_stride(rec_tokens))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _i32(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+        raise TypeError(f"{name} must be a contiguous int32 device tensor")
+    return t
+
+
+class Pools:
+    """Layer-indexed state and record pools (torch tensors, caller-owned).
+
+    state: [L][slots][HV][V][K] fp32 or bf16 (one tensor, or a list of
+    per-layer [slots][HV][V][K] tensors); rec: [L][rec_slots][HV][stride] fp32
+    with stride = rec_stride(rec_tokens).
+    """
+
+    def __init__(self, state, rec, num_k_heads: int, rec_tokens: int):
+        self.state = list(state) if not torch.is_tensor(state) else [state[i] for i in range(state.shape[0])]
+        self.rec = list(rec) if not torch.is_tensor(rec) else [rec[i] for i in range(rec.shape[0])]
+        s0 = self.state[0]
+        self.num_layers = len(self.state)
+        self.num_slots, self.hv, V, K = s0.shape
+        self.hk = num_k_heads
+        self.rec_tokens = rec_tokens
+        self.dtype = s0.dtype
+        if self.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("state pools are fp32 or bf16")
+        self.num_rec_slots = self.rec[0].shape[0]
+        st = gdn_pools()
+        st.num_layers = self.num_layers
+        st.num_v_heads = self.hv
+        st.num_k_heads = num_k_heads
+        st.head_k_dim = K
+        st.head_v_dim = V
+        st.state_dtype = GDN_STATE_BF16 if self.dtype == torch.bfloat16 else GDN_STATE_F32
+        st.num_state_slots = self.num_slots
+        st.num_rec_slots = self.num_rec_slots
+        st.rec_tokens = rec_tokens
+        for i, (s, r) in enumerate(zip(self.state, self.rec)):
+            if not (s.is_contiguous() and r.is_contiguous()):
+                raise TypeError("pools must be contiguous")
+            st.state[i] = s.data_ptr()
+            st.rec[i] = r.data_ptr()
+        self.c = st
+
+    @staticmethod
+    def alloc_records(num_layers, num_rec_slots, hv, rec_tokens, device="cuda"):
+        return torch.zeros((num_layers, num_rec_slots, hv, rec_stride(rec_tokens)),
+                           dtype=torch.float32, device=device)
+
+
+def _io(q, k, v, a_log, beta, out, scale) -> gdn_verify_io:
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+            raise TypeError(f"{name} must be a bf16 [tokens][heads][128] view, feature-contiguous")
+    if a_log.dtype != torch.float32 or beta.dtype != torch.float32 or a_log.dim() != 2 \
+            or a_log.stride(1) != 1 or beta.stride() != a_log.stride():
+        raise TypeError("a_log and beta must be fp32 [tokens][HV] with the same strides")
+    if out.dtype != torch.float32 or out.dim() != 3 or out.stride(2) != 1:
+        raise TypeError("out must be an fp32 [tokens][HV][128] view, feature-contiguous")
+    io = gdn_verify_io()
+    io.q, io.q_tok_stride, io.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
+    io.k, io.k_tok_stride, io.k_head_stride = k.data_ptr(), k.stride(0), k.stride(1)
+    io.v, io.v_tok_stride, io.v_head_stride = v.data_ptr(), v.stride(0), v.stride(1)
+    io.a_log, io.beta, io.gate_tok_stride = a_log.data_ptr(), beta.data_ptr(), a_log.stride(0)
+    io.out, io.out_tok_stride, io.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
+    io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a_log.shape[0], out.shape[0])
+    io.scale = float(scale)
+    return io
+
+
+def gdn_verify(pools: Pools, layer: int, state_slot, rec_slot, tok_start, win_len, rec_base,
+               q, k, v, a_log, beta, out, *, scale=1.0, err_flags=None, stream=None) -> int:
+    lib = load_library()
+    io = _io(q, k, v, a_log, beta, out, scale)
+    n = state_slot.shape[0]
+    return _check(lib.gdn_verify(C.byref(pools.c), layer, n, _ptr(_i32(state_slot, "state_slot")),
+                                 _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(tok_start, "tok_start")),
+                                 _ptr(_i32(win_len, "win_len")), _ptr(_i32(rec_base, "rec_base")),
+                                 C.byref(io), _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_native_window(pools: Pools, layer: int, state_slot, tok_start, win_len,
+                      q, k, v, a_log, beta, out, snap, *, scale=1.0, err_flags=None,
+                      stream=None) -> int:
+    lib = load_library()
+    io = _io(q, k, v, a_log, beta, out, scale)
+    if snap.dtype != pools.dtype or not snap.is_contiguous():
+        raise TypeError("snap must be contiguous with the pool's dtype")
+    n = state_slot.shape[0]
+    return _check(lib.gdn_native_window(C.byref(pools.c), layer, n,
+                                        _ptr(_i32(state_slot, "state_slot")),
+                                        _ptr(_i32(tok_start, "tok_start")),
+                                        _ptr(_i32(win_len, "win_len")), C.byref(io), _ptr(snap),
+                                        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_commit_all_layers(pools: Pools, src_slot, dst_slot, rec_slot, n_accept, bnd_len=None,
+                          bnd_slot=None, *, err_flags=None, stream=None) -> int:
+    lib = load_library()
+    n = src_slot.shape[0]
+    return _check(lib.gdn_commit_all_layers(
+        C.byref(pools.c), n, _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
+        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
+        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
+        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_native_accept(pools: Pools, snaps, dst_slot, n_accept, *, err_flags=None,
+                      stream=None) -> int:
+    lib = load_library()
+    arr = (C.c_void_p * len(snaps))(*[s.data_ptr() for s in snaps])
+    return _check(lib.gdn_native_accept(C.byref(pools.c), arr, dst_slot.shape[0],
+                                        _ptr(_i32(dst_slot, "dst_slot")),
+                                        _ptr(_i32(n_accept, "n_accept")),
+                                        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_align_plan(num_computed, n_accept, block_table, block_size: int, max_accept: int,
+                   src_slot, dst_slot, bnd_len, bnd_slot, *, err_flags=None, stream=None) -> int:
+    lib = load_library()
+    bt = _i32(block_table, "block_table")
+    return _check(lib.gdn_align_plan(
+        num_computed.shape[0], _ptr(_i32(num_computed, "num_computed")),
+        _ptr(_i32(n_accept, "n_accept")), _ptr(bt), bt.stride(0), bt.shape[1], block_size,
+        max_accept, _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
+        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
+        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))

@@ -1,0 +1,78 @@
+// gdn_device.hpp -- device helpers for the gfx950 verify / commit kernels.
+//
+// Wave64 on CDNA4: reductions over 8 or 16 consecutive lanes use DPP lane
+// permutes inside one 16-lane DPP row (quad permutes, then the half-row and
+// row mirrors), never LDS. Each step adds a lane's value to its partner's;
+// IEEE addition is commutative, so after every step all lanes of the group
+// hold the bit-identical sum. Every kernel built from these helpers is
+// compiled with floating-point contraction off: an fma is issued only where
+// the method fuses one.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kDim = 128;          // K = V = 128
+constexpr int kHeadElems = kDim * kDim;
+constexpr int kThreads = 256;      // four wave64s per workgroup
+constexpr float kNormEps = 1e-6f;  // inside the square root of the L2 norm
+
+// Row-error bits, the values the C ABI documents.
+constexpr int kRowSlot = 1, kRowWin = 2, kRowN = 4, kRowBnd = 8, kRowTable = 16,
+              kRowRec = 32, kRowPos = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 ------------------------------------------------------------------
+// A bf16 value is the top half of an fp32 value: widening is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- DPP lane exchange -----------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i inside each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 lanes 8m..8m+7; every one of them returns the same bits.
+__device__ __forceinline__ float sum8(float x) {
+    x = x + dpp<kDppQuadXor1>(x);
+    x = x + dpp<kDppQuadXor2>(x);
+    x = x + dpp<kDppRowHalfMirror>(x);
+    return x;
+}
+
+// Sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float sum16(float x) {
+    x = sum8(x);
+    return x + dpp<kDppRowMirror>(x);
+}
+
+// ---- vector memory ---------------------------------------------------------
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st4_nt(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
+}  // namespace gdn

@@ -1,0 +1,84 @@
+// gdn_kernels.hpp -- kernel parameter blocks and launchers (internal to the
+// library; the public interface is include/gdn_replay.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_replay.h"
+
+namespace gdn {
+
+// One layer's verify (or native snapshot window). Passed by value as the
+// kernel argument block.
+struct VerifyParams {
+    const void* state;        // layer pool [slots][HV][V][K]
+    float* rec;               // layer record pool [rec_slots][HV][rec_stride]
+    void* snap;               // native only: [rows][HV][T][V][K]
+    const int32_t* state_slot;
+    const int32_t* rec_slot;  // verify only
+    const int32_t* tok_start;
+    const int32_t* win_len;
+    const int32_t* rec_base;  // verify only, may be null
+    const uint16_t* q; int64_t q_ts, q_hs;
+    const uint16_t* k; int64_t k_ts, k_hs;
+    const uint16_t* v; int64_t v_ts, v_hs;
+    const float* a_log; const float* beta; int64_t g_ts;
+    float* out; int64_t o_ts, o_hs;
+    int64_t num_tokens;
+    int64_t rec_stride;       // floats per (record slot, value head)
+    int32_t* err;
+    int32_t num_rows, hv, group, num_slots, num_rec_slots, T;
+    float scale;
+};
+
+// The all-layer commit.
+struct CommitParams {
+    void* state[GDN_MAX_LAYERS];
+    const float* rec[GDN_MAX_LAYERS];
+    const int32_t* src;
+    const int32_t* dst;
+    const int32_t* rec_slot;
+    const int32_t* n;
+    const int32_t* bnd_len;   // align mode only
+    const int32_t* bnd_slot;
+    int32_t* err;
+    int64_t rec_stride;
+    int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
+};
+
+// The native baseline's accepted-state copy.
+struct AcceptParams {
+    void* state[GDN_MAX_LAYERS];
+    const void* snap[GDN_MAX_LAYERS];
+    const int32_t* dst;
+    const int32_t* n;
+    int32_t* err;
+    int32_t num_layers, num_rows, hv, num_slots, T;
+};
+
+struct PlanParams {
+    const int32_t* p0;
+    const int32_t* n;
+    const int32_t* table;
+    int64_t table_stride;
+    int32_t* src;
+    int32_t* dst;
+    int32_t* bnd_len;
+    int32_t* bnd_slot;
+    int32_t* err;
+    int32_t num_rows, cols, block, max_n;
+};
+
+// Launchers: return the hipError_t of the launch.
+hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s);
+hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s);
+hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s);
+hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s);
+hipError_t launch_align_plan(const PlanParams& p, hipStream_t s);
+
+// Dynamic LDS of the verify kernel for record capacity T (bytes).
+inline size_t verify_lds_bytes(int T) { return sizeof(float) * (3 * (size_t)T * 128 + 2 * (size_t)T); }
+inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + (size_t)T); }
+
+}  // namespace gdn

@@ -1,0 +1,240 @@
+/*
+ * gdn_replay.h -- C ABI of the MI355X (gfx950) verify-and-commit library for
+ * Gated DeltaNet recurrent state under speculative (MTP) decoding.
+ *
+ * The method, cited by page title and section:
+ *   [vLLM] vLLM PR "[Spec Decode][Qwen4Exp] RecoverSSM for Qwen GDN and the
+ *          PLE short conv" -- Purpose (verify from a read-only checkpoint,
+ *          fp32 per-token record of correction, normalised key and gate;
+ *          commit after sampling replays only the accepted tokens and writes
+ *          the state once, plus the block-boundary state in align mode;
+ *          padding rows have a null slot and a zero-length window), Commits
+ *          items 2, 3 and 6 (strided q/k/v views written straight into the
+ *          layer output; a window ending on a boundary stays in its last
+ *          token's block; final folds before boundary folds), Test Plan
+ *          (bf16 state; malformed-input rejection), Test Result (the commit
+ *          replays h = fma(correction, key, h * decay) and equals the native
+ *          per-token state bit for bit).
+ *   [TS]   tokenspeed PR "feat: add Qwen3.5 GDN ReplaySSM" -- Summary and
+ *          Implementation (one all-layer commit launch; layer-indexed state
+ *          and replay pools; a cooperative 4-warp block per 128x128 head).
+ *   [LMD]  lmdeploy PR #5028 (opt-in ReplaySSM) -- Performance test settings
+ *          (16-token replay buffer; 64-token blocks; fp32 SSM state) and the
+ *          file list (cursor commits and checkpoint flushing).
+ *   [GDN]  Yang, Kautz, Hatamizadeh, "Gated Delta Networks" (ICLR 2025): the
+ *          per-token gated delta rule.
+ *
+ * Per token t of one value head (K = V = 128, all fp32):
+ *   k_hat = k / sqrt(|k|^2 + 1e-6),  q_tilde = scale * q / sqrt(|q|^2 + 1e-6)
+ *   g = exp(a)  (a = log-gate),  h' = g * h
+ *   delta = beta * (v - h' k_hat),  h = fma(delta, k_hat^T, h')
+ *   o_t = h q_tilde
+ * Value head hv reads key head hv / (HV / HK).
+ *
+ * Conventions for every entry point:
+ *   - All pointers named "device" are HIP device memory owned by the caller.
+ *     The library allocates nothing and keeps no pointer after returning.
+ *   - gdn_pools and gdn_verify_io are host structs, read during the call.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream), never synchronise the host, and are capturable in a HIP graph.
+ *   - Host-checkable errors return a negative gdn_status and launch nothing.
+ *   - Per-row device data out of range makes the kernel skip that row and OR
+ *     a GDN_ROW_* bit into *err_flags (device int32, may be NULL). The caller
+ *     clears *err_flags.
+ *   - Preconditions not checked: no two live rows share a state, destination,
+ *     boundary or record slot; buffers are as large as the sizes say.
+ */
+#ifndef GDN_REPLAY_H
+#define GDN_REPLAY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+#define GDN_MAX_LAYERS 64      /* layers per pool set */
+#define GDN_HEAD_DIM 128       /* K = V = 128 */
+#define GDN_MAX_REC_TOKENS 32  /* record capacity T per row */
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,    /* a required pointer is NULL */
+    GDN_ERR_SHAPE = -2,   /* a size or index argument is out of range */
+    GDN_ERR_DTYPE = -3,   /* unsupported state dtype */
+    GDN_ERR_ALIGN = -4,   /* a pointer or stride breaks the 16-byte rule */
+    GDN_ERR_LAUNCH = -5   /* the HIP launch failed */
+} gdn_status;
+
+typedef enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 } gdn_state_dtype;
+
+/* Device row-error bits (OR'ed into *err_flags). */
+enum {
+    GDN_ROW_SLOT = 1,    /* a state / destination slot >= num_state_slots */
+    GDN_ROW_WIN = 2,     /* window: w < 0, rec_base < 0, rec_base + w > T, or tokens out of range */
+    GDN_ROW_N = 4,       /* accepted count < 0 or > T, or n > 0 with a null destination */
+    GDN_ROW_BND = 8,     /* boundary length not 0 and not in (0, n), bad boundary slot,
+                            or (plan) more than one block boundary inside the window */
+    GDN_ROW_TABLE = 16,  /* (plan) block-table column out of range or empty where needed */
+    GDN_ROW_REC = 32,    /* record slot < 0 or >= num_rec_slots for a live row */
+    GDN_ROW_POS = 64     /* (plan) num_computed < 1 */
+};
+
+/*
+ * Layer-indexed state and record pools ([TS] Implementation; [vLLM] Purpose).
+ *
+ * state[l]: device, layer l's checkpoint pool, [num_state_slots][HV][V][K],
+ *   K contiguous, fp32 or bf16 per state_dtype. 16-byte aligned.
+ * rec[l]: device, layer l's record pool, [num_rec_slots][HV][rec_stride]
+ *   fp32 with rec_stride = gdn_rec_stride(rec_tokens). The block of one
+ *   (record slot, value head) is
+ *     delta[T][V] | k_hat[T][K] | gate[T] | zero padding to 4 floats,
+ *   position p of the window (ring position in ring mode) at index p.
+ *   16-byte aligned. Records live only from a step's verify to its commit.
+ */
+typedef struct gdn_pools {
+    int32_t num_layers;       /* 1..GDN_MAX_LAYERS */
+    int32_t num_v_heads;      /* HV >= 1 */
+    int32_t num_k_heads;      /* HK >= 1, HV % HK == 0 */
+    int32_t head_k_dim;       /* must be 128 */
+    int32_t head_v_dim;       /* must be 128 */
+    int32_t state_dtype;      /* gdn_state_dtype */
+    int32_t num_state_slots;  /* >= 1 */
+    int32_t num_rec_slots;    /* >= 1 */
+    int32_t rec_tokens;       /* T, 1..GDN_MAX_REC_TOKENS */
+    int32_t reserved;         /* set to 0 */
+    void* state[GDN_MAX_LAYERS];
+    float* rec[GDN_MAX_LAYERS];
+} gdn_pools;
+
+/*
+ * Per-token inputs and outputs of one layer's verify ([vLLM] Commits item 2:
+ * strided q/k/v views of the short-conv output, output written in place).
+ * Strides are in elements; the innermost (feature) dimension is contiguous.
+ *   q, k: device bf16 bits, [tokens][HK][K];  v: device bf16 bits, [tokens][HV][V].
+ *     Base pointers 16-byte aligned, strides multiples of 8 elements.
+ *   a_log, beta: device fp32 [tokens][HV] (head stride 1); a_log is the
+ *     log-gate (the decay is exp(a_log)), beta the write strength.
+ *   out: device fp32 [tokens][HV][V]; 16-byte aligned, strides multiples of 4.
+ *   num_tokens: rows address tokens [tok_start, tok_start + w) < num_tokens.
+ *   scale: multiplies the normalised query (1 = the plain o_t = S_t q_t).
+ */
+typedef struct gdn_verify_io {
+    const uint16_t* q;  int64_t q_tok_stride, q_head_stride;
+    const uint16_t* k;  int64_t k_tok_stride, k_head_stride;
+    const uint16_t* v;  int64_t v_tok_stride, v_head_stride;
+    const float* a_log; const float* beta; int64_t gate_tok_stride;
+    float* out;         int64_t out_tok_stride, out_head_stride;
+    int64_t num_tokens;
+    float scale;
+    int32_t reserved;   /* set to 0 */
+} gdn_verify_io;
+
+/*
+ * gdn_verify -- verify one layer's draft windows from the read-only
+ * checkpoint ([vLLM] Purpose; Test Plan: checkpoint untouched).
+ *
+ * For each row b (all arrays device int32 [num_rows]):
+ *   state_slot[b] < 0 or win_len[b] == 0: the row is padding and nothing at
+ *     all is read or written for it ([vLLM] Purpose, graph padding rows).
+ *   Otherwise the kernel loads S = state[layer][state_slot[b]] (bf16 widened
+ *   exactly), first replays the rec_base[b] records already at positions
+ *   0..rec_base-1 of record slot rec_slot[b] (ring mode, [LMD]; rec_base may
+ *   be NULL = all zero), then runs tokens tok_start[b] .. tok_start[b]+w-1:
+ *   writes o_t into io->out and the record (delta, k_hat, gate) at position
+ *   rec_base + t. The state pool is never written.
+ * Errors: GDN_ERR_* as in the conventions; device rows with a bad slot,
+ * window or record slot are skipped with GDN_ROW_SLOT / _WIN / _REC.
+ */
+int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
+                   const int32_t* state_slot, const int32_t* rec_slot,
+                   const int32_t* tok_start, const int32_t* win_len,
+                   const int32_t* rec_base, const gdn_verify_io* io,
+                   int32_t* err_flags, void* stream);
+
+/*
+ * gdn_commit_all_layers -- after sampling, replay each row's accepted prefix
+ * and write the state once, for every layer in one launch ([TS] Summary;
+ * [vLLM] Purpose, Test Result).
+ *
+ * One 4-wave workgroup per (layer, row, value head). For row b (device int32
+ * arrays [num_rows]):
+ *   n = n_accept[b]; if n == 0 or src_slot[b] < 0 nothing is read or written.
+ *   h = state[l][src_slot[b]]; for t < n: h = fma(delta_t, k_hat_t^T, h * g_t)
+ *   with the records of rec_slot[b]; the final h is written to dst_slot[b]
+ *   (dst == src: in place). bf16 pools round once, to nearest even, here.
+ *   Align mode (bnd_len and bnd_slot non-NULL): when 0 < bnd_len[b] < n the
+ *   state after bnd_len[b] tokens is also written to bnd_slot[b], after the
+ *   final state and from the same single read of the source, and not at all
+ *   when bnd_slot[b] == dst_slot[b] ([vLLM] Commits item 6). Each workgroup
+ *   reads its whole source head before its first store, so a boundary or
+ *   final slot equal to the source slot is safe.
+ * Errors: GDN_ROW_SLOT, _N, _BND, _REC for bad device rows (row skipped).
+ */
+int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
+                              const int32_t* src_slot, const int32_t* dst_slot,
+                              const int32_t* rec_slot, const int32_t* n_accept,
+                              const int32_t* bnd_len, const int32_t* bnd_slot,
+                              int32_t* err_flags, void* stream);
+
+/*
+ * gdn_align_plan -- align-mode slots of each row from its block table
+ * ([vLLM] Purpose; Commits items 3 and 6).
+ *
+ * Row b has a checkpoint covering num_computed[b] = p0 >= 1 tokens and
+ * n = n_accept[b] (0..max_accept) accepted tokens. A state covering m tokens
+ * lives in block column (m - 1) / block_size of block_table (device int32,
+ * row stride bt_row_stride elements, bt_cols columns, -1 = unallocated):
+ *   src_slot = table[(p0-1)/B];  dst_slot = table[(p0+n-1)/B] (-1 if n == 0);
+ *   if the window crosses a block boundary after t < n tokens ((p0+t) % B == 0)
+ *   bnd_len = t and bnd_slot = table[(p0+t-1)/B] (else 0 and -1); a boundary
+ *   slot equal to the final slot is dropped.
+ * Outputs: device int32 [num_rows]. Rows with an error (GDN_ROW_POS, _N, _BND
+ * for a second boundary, _TABLE) get all four outputs null.
+ * Host errors: block_size < 1, max_accept < 0, bt_cols < 1, strides < bt_cols.
+ */
+int32_t gdn_align_plan(int32_t num_rows, const int32_t* num_computed,
+                       const int32_t* n_accept, const int32_t* block_table,
+                       int64_t bt_row_stride, int32_t bt_cols, int32_t block_size,
+                       int32_t max_accept, int32_t* src_slot, int32_t* dst_slot,
+                       int32_t* bnd_len, int32_t* bnd_slot, int32_t* err_flags,
+                       void* stream);
+
+/*
+ * gdn_native_window -- the baseline being replaced: the same verify
+ * arithmetic, but the state after every draft token is written out
+ * ([vLLM] Purpose: native spec decode snapshots the full state after every
+ * draft position; [TS] Motivation). Bit-identical outputs to gdn_verify.
+ *
+ * snap: device, [num_rows][HV][T][V][K] in the pool's state dtype (T =
+ *   pools->rec_tokens); snap[b][h][t] = state after token t of row b, rounded
+ *   to bf16 for bf16 pools. 16-byte aligned. No record is written.
+ * Rows: as gdn_verify without record slot and ring base.
+ */
+int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_rows,
+                          const int32_t* state_slot, const int32_t* tok_start,
+                          const int32_t* win_len, const gdn_verify_io* io, void* snap,
+                          int32_t* err_flags, void* stream);
+
+/*
+ * gdn_native_accept -- the baseline's state copy: for every layer, row b
+ * with n = n_accept[b] >= 1 copies snap_layers[l][b][h][n-1] into
+ * state[l][dst_slot[b]][h]. snap_layers: host array of num_layers device
+ * pointers laid out as in gdn_native_window.
+ */
+int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers,
+                          int32_t num_rows, const int32_t* dst_slot,
+                          const int32_t* n_accept, int32_t* err_flags, void* stream);
+
+/* Floats per (record slot, value head) block: T*(V+K) + T rounded up to 4. */
+int64_t gdn_rec_stride(int32_t rec_tokens);
+
+const char* gdn_status_string(int32_t status);
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_REPLAY_H */

@@ -87,7 +87,11 @@ def _load():
 
 
 def default_threads() -> int:
-    """Host threads for the OpenMP loops: the cores this process may use."""
+    """Host threads for the OpenMP loops: OMP_NUM_THREADS when set, else the
+    cores this process may use."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
     try:
         return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover

@@ -94,11 +94,14 @@ int gdno_native_heads_##SUF(int nheads, int K, int V, int T,                    
         R* qt = (R*)malloc(sizeof(R) * K);                                              \
         R* kh = (R*)malloc(sizeof(R) * K);                                              \
         R* loc = (R*)malloc(sizeof(R) * VK * (T + 1));                                  \
-        if (!h || !qt || !kh || !loc) {                                                 \
+        int ok = h && qt && kh && loc;                                                  \
+        if (!ok) {                                                                      \
             _Pragma("omp atomic write") bad = 1;                                        \
-        } else {                                                                        \
+        }                                                                               \
+        {   /* every thread reaches the worksharing loop */                             \
             _Pragma("omp for schedule(dynamic, 4)")                                     \
             for (int i = 0; i < nheads; ++i) {                                          \
+                if (!ok) continue;                                                      \
                 const long tk = (long)i * T;                                            \
                 /* keep every state locally: loc[0] = S_0, loc[j] = S_j */              \
                 memcpy(loc, S0 + i * VK, sizeof(R) * VK);                               \
@@ -192,7 +195,7 @@ void gdno_f32_to_bf16_rne(long n, const float* in, uint16_t* out)
  *
  * Error bits (the library's documented row-error values): 4 = n out of range,
  * 8 = more than one boundary in the window, 16 = block-table column out of
- * range or an empty (negative) table entry where a slot is needed, 1 = p0 < 1.
+ * range or an empty (negative) table entry where a slot is needed, 64 = p0 < 1.
  * A row with an error gets src = dst = bnd_slot = -1, bnd_len = 0.
  * Returns the OR of all row errors.
  * ------------------------------------------------------------------------- */
@@ -205,7 +208,7 @@ int gdno_align_plan(int rows, const int* p0, const int* n, const int* table,
         const int* tb = table + (long)b * table_row_stride;
         int err = 0;
         int s = -1, d = -1, bl = 0, bs = -1, nb = 0;
-        if (p0[b] < 1) err |= 1;
+        if (p0[b] < 1) err |= 64;
         if (n[b] < 0 || n[b] > max_n) err |= 4;
         if (!err) {
             long col = ((long)p0[b] - 1) / block;

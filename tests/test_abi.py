@@ -1,0 +1,176 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/gdn_replay.h declares, and rejects malformed host arguments with the
+documented status before any HIP call (vLLM RecoverSSM PR, Test Plan:
+malformed-input rejection). Only calls that validation rejects are made."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import gated_deltanet_speculative_gdn_amd as g
+from gated_deltanet_speculative_gdn_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return g.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_version_and_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(lib.gdn_status_string(s), bytes)
+    assert lib.gdn_status_string(-4).decode().startswith("a pointer or stride")
+
+
+def test_record_stride():
+    # delta[T][128] | k_hat[T][128] | gate[T] padded to 4 floats
+    assert g.rec_stride(4) == 4 * 256 + 4
+    assert g.rec_stride(16) == 16 * 256 + 16
+    assert g.rec_stride(1) == 256 + 4
+    assert g.rec_stride(5) == 5 * 256 + 8
+    assert g.rec_stride(0) == 0
+
+
+def good_pools():
+    p = B.gdn_pools()
+    p.num_layers, p.num_v_heads, p.num_k_heads = 2, 4, 2
+    p.head_k_dim = p.head_v_dim = 128
+    p.state_dtype = 0
+    p.num_state_slots, p.num_rec_slots, p.rec_tokens = 8, 8, 4
+    for i in range(2):
+        p.state[i] = 0x10000 + i * 0x100000   # never dereferenced: calls below are rejected
+        p.rec[i] = 0x20000 + i * 0x100000
+    return p
+
+
+def good_io():
+    io = B.gdn_verify_io()
+    io.q, io.q_tok_stride, io.q_head_stride = 0x30000, 512, 128
+    io.k, io.k_tok_stride, io.k_head_stride = 0x40000, 512, 128
+    io.v, io.v_tok_stride, io.v_head_stride = 0x50000, 512, 128
+    io.a_log, io.beta, io.gate_tok_stride = 0x60000, 0x70000, 4
+    io.out, io.out_tok_stride, io.out_head_stride = 0x80000, 512, 128
+    io.num_tokens, io.scale = 16, 1.0
+    return io
+
+
+ROWS = C.c_void_p(0x90000)
+
+
+def verify(lib, pools, io, layer=0, rows=4, slot=ROWS, rec=ROWS):
+    return lib.gdn_verify(C.byref(pools) if pools is not None else None, layer, rows, slot, rec,
+                          ROWS, ROWS, None, C.byref(io) if io is not None else None, None, None)
+
+
+def test_verify_zero_rows_is_ok_without_launch(lib):
+    assert verify(lib, good_pools(), good_io(), rows=0) == OK
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p, io: None, None),
+    (lambda p, io: setattr(p, "head_k_dim", 64), E_SHAPE),
+    (lambda p, io: setattr(p, "head_v_dim", 256), E_SHAPE),
+    (lambda p, io: setattr(p, "num_k_heads", 3), E_SHAPE),
+    (lambda p, io: setattr(p, "num_layers", 0), E_SHAPE),
+    (lambda p, io: setattr(p, "num_layers", 65), E_SHAPE),
+    (lambda p, io: setattr(p, "rec_tokens", 0), E_SHAPE),
+    (lambda p, io: setattr(p, "rec_tokens", 33), E_SHAPE),
+    (lambda p, io: setattr(p, "num_state_slots", 0), E_SHAPE),
+    (lambda p, io: setattr(p, "state_dtype", 2), E_DTYPE),
+    (lambda p, io: p.state.__setitem__(0, 0), E_NULL),
+    (lambda p, io: p.rec.__setitem__(0, 0), E_NULL),
+    (lambda p, io: p.state.__setitem__(0, 0x10004), E_ALIGN),
+    (lambda p, io: setattr(io, "q", None), E_NULL),
+    (lambda p, io: setattr(io, "out", None), E_NULL),
+    (lambda p, io: setattr(io, "q", 0x30008), E_ALIGN),
+    (lambda p, io: setattr(io, "k_tok_stride", 516), E_ALIGN),
+    (lambda p, io: setattr(io, "out_head_stride", 130), E_ALIGN),
+    (lambda p, io: setattr(io, "a_log", 0x60002), E_ALIGN),
+    (lambda p, io: setattr(io, "num_tokens", -1), E_SHAPE),
+    (lambda p, io: setattr(io, "v_head_stride", -8), E_SHAPE),
+])
+def test_verify_rejects_malformed(lib, mutate, status):
+    p, io = good_pools(), good_io()
+    mutate(p, io)
+    if status is None:
+        # the unmodified arguments are valid: only check with zero rows (no launch)
+        assert verify(lib, p, io, rows=0) == OK
+        return
+    assert verify(lib, p, io) == status
+
+
+def test_verify_rejects_bad_layer_and_rows(lib):
+    assert verify(lib, good_pools(), good_io(), layer=2) == E_SHAPE
+    assert verify(lib, good_pools(), good_io(), layer=-1) == E_SHAPE
+    assert verify(lib, good_pools(), good_io(), rows=-1) == E_SHAPE
+    assert verify(lib, None, good_io()) == E_NULL
+    assert verify(lib, good_pools(), None) == E_NULL
+    assert verify(lib, good_pools(), good_io(), slot=None) == E_NULL
+
+
+def commit(lib, pools, rows=4, bl=None, bs=None, src=ROWS):
+    return lib.gdn_commit_all_layers(C.byref(pools), rows, src, ROWS, ROWS, ROWS, bl, bs, None,
+                                     None)
+
+
+def test_commit_rejects_malformed(lib):
+    assert commit(lib, good_pools(), rows=0) == OK
+    assert commit(lib, good_pools(), rows=-3) == E_SHAPE
+    assert commit(lib, good_pools(), src=None) == E_NULL
+    assert commit(lib, good_pools(), bl=ROWS, bs=None) == E_NULL
+    p = good_pools()
+    p.rec[1] = 0                      # every layer's pools must be present
+    assert commit(lib, p) == E_NULL
+    p = good_pools()
+    p.state[1] = 0x10008
+    assert commit(lib, p) == E_ALIGN
+    p = good_pools()
+    p.num_v_heads = 5
+    assert commit(lib, p) == E_SHAPE
+
+
+def test_align_plan_rejects_malformed(lib):
+    def plan(rows=4, stride=8, cols=8, block=64, max_n=16, table=ROWS):
+        return lib.gdn_align_plan(rows, ROWS, ROWS, table, stride, cols, block, max_n,
+                                  ROWS, ROWS, ROWS, ROWS, None, None)
+    assert plan(rows=0) == OK
+    assert plan(block=0) == E_SHAPE
+    assert plan(max_n=-1) == E_SHAPE
+    assert plan(cols=0) == E_SHAPE
+    assert plan(stride=4, cols=8) == E_SHAPE
+    assert plan(table=None) == E_NULL
+
+
+def test_native_rejects_malformed(lib):
+    p, io = good_pools(), good_io()
+    assert lib.gdn_native_window(C.byref(p), 0, 4, ROWS, ROWS, ROWS, C.byref(io), None, None,
+                                 None) == E_NULL
+    assert lib.gdn_native_window(C.byref(p), 0, 4, ROWS, ROWS, ROWS, C.byref(io),
+                                 C.c_void_p(0xA0004), None, None) == E_ALIGN
+    snaps = (C.c_void_p * 2)(0xB0000, 0)
+    assert lib.gdn_native_accept(C.byref(p), snaps, 4, ROWS, ROWS, None, None) == E_NULL
+    snaps = (C.c_void_p * 2)(0xB0000, 0xC0000)
+    assert lib.gdn_native_accept(C.byref(p), snaps, 0, ROWS, ROWS, None, None) == OK

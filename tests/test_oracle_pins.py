@@ -351,7 +351,7 @@ def test_align_plan_errors():
     p0 = np.array([0, 5, 6, 127, 60], np.int32)
     n = np.array([1, 9, 4, 2, 4], np.int32)   # row 3 needs the empty column 2
     src, dst, bl, bs, err = oracle.align_plan(p0, n, table, 64, 8)
-    assert err.tolist() == [1, 4, 0, 16, 0]
+    assert err.tolist() == [64, 4, 0, 16, 0]
     assert (src[0], dst[0]) == (-1, -1) and (src[3], dst[3]) == (-1, -1)
     # a window longer than a block crosses two boundaries: rejected
     t2 = np.array([[1, 2, 3, 4]], np.int32)

@@ -1,0 +1,481 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (vLLM RecoverSSM PR, Test Plan and Test Result; the tolerance is the
+1e-5 relative error the method's fp32 states and outputs must meet):
+  * fp32 states, outputs and records: normwise relative error per block
+    (max|x - y| / max|y| over one state head, one output vector, one record
+    vector) <= 1e-5 against the oracle's native per-token rule;
+  * the commit against the oracle's replay of the GPU's own records: bit-exact
+    (the replay is elementwise, so there is no reduction order to differ in);
+  * slots, plans and write sets: bit-exact;
+  * one-hot queries and keys with gates in {1, 0}: every reduction has one
+    non-zero term, so GPU and oracle agree exactly;
+  * bf16 pools: verify bit-identical to the fp32 path on the widened state; the
+    commit equal to the once-rounded (RNE) oracle replay of the GPU records,
+    and within one bf16 ulp (+ the fp32 tolerance) of the oracle's fp32 state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pool as OP
+from gated_deltanet_speculative_gdn_amd import workloads as W
+from gpu_harness import Harness, dev_i32
+
+TOL = 1e-5
+pytestmark = pytest.mark.gpu
+
+
+def bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x).view(np.uint32 if x.dtype == np.float32 else np.uint16)
+
+
+def assert_bitwise(x, y, what=""):
+    x, y = np.asarray(x), np.asarray(y)
+    assert x.shape == y.shape, (what, x.shape, y.shape)
+    bad = bits(x) != bits(y)
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} differ"
+
+
+def assert_close(x, y, ndim, what=""):
+    err = OP.relerr_blocks(x, y, ndim)
+    assert err <= TOL, f"{what}: normwise relative error {err:.3e} > {TOL}"
+
+
+def pool_bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def check_layer(h, layer, rows, n, pre_state, *, T=None, bnd=None, dst=None, check_out=True):
+    """Compare one layer's outputs, records and committed states for ``rows``
+    against the oracle. ``n`` [R] accepted counts; ``bnd`` optional [R]
+    boundary lengths (0 = none) with slots in ``bnd[1]``; ``dst`` [R] slots
+    holding the final state (default: the row's state slot)."""
+    wl, s = h.wl, h.s
+    rows = np.asarray(rows)
+    n = np.asarray(n)
+    keep = [n]
+    if bnd is not None:
+        keep.append(np.where(bnd[0] > 0, bnd[0], -1))
+    keep = np.stack(keep, 1)
+    g, res = OP.run_layer(wl, layer, rows, keep=keep, T=T, state=pre_state)
+    w = g["w"]
+    Tw = g["q"].shape[1]
+    valid = np.arange(Tw)[None, :] < w[:, None]
+    if check_out:
+        o = h.outputs(layer, rows, T)
+        assert_close(np.where(valid[..., None], o, 0), np.where(valid[..., None], res.o, 0), 1,
+                     f"layer {layer} outputs")
+    d, kh, gg = h.records(layer, rows)
+    d, kh, gg = d[:, :Tw], kh[:, :Tw], gg[:, :Tw]
+    assert_close(np.where(valid[..., None], d, 0), res.rec_delta, 1, f"layer {layer} corrections")
+    assert_close(np.where(valid[..., None], kh, 0), res.rec_khat, 1, f"layer {layer} keys")
+    assert_close(np.where(valid, gg, 0), res.rec_g, 1, f"layer {layer} gates")
+    n_h = np.repeat(n, s.hv)
+    # final state: within tolerance of the native rule, bit-exact vs replay of the GPU records
+    dst = wl.state_slot[rows] if dst is None else np.asarray(dst)
+    live = n > 0
+    if live.any():
+        got = h.heads(layer, dst[live])
+        live_h = np.repeat(live, s.hv)
+        d_f = np.where(valid[..., None], d, 0).astype(np.float32)
+        k_f = np.where(valid[..., None], kh, 0).astype(np.float32)
+        g_f = np.where(valid, gg, 0).astype(np.float32)
+        rep = oracle.replay_heads(g["S0"][live_h], n_h[live_h], d_f[live_h], k_f[live_h],
+                                  g_f[live_h])
+        if h.wl.state_dtype == torch.float32:
+            assert_close(got, res.kept[live_h, 0], 2, f"layer {layer} final states")
+            assert_bitwise(got, rep, f"layer {layer} final state vs replay of GPU records")
+        else:
+            check_bf16(h, layer, dst[live], rep, res.kept[live_h, 0], "final")
+        if bnd is not None:
+            bl, bs = np.asarray(bnd[0]), np.asarray(bnd[1])
+            has = bl > 0
+            if has.any():
+                has_h = np.repeat(has, s.hv)
+                gotb = h.heads(layer, bs[has])
+                repb = oracle.replay_heads(g["S0"][has_h], np.repeat(bl[has], s.hv), d_f[has_h],
+                                           k_f[has_h], g_f[has_h])
+                if h.wl.state_dtype == torch.float32:
+                    assert_close(gotb, res.kept[has_h, 1], 2, f"layer {layer} boundary states")
+                    assert_bitwise(gotb, repb, f"layer {layer} boundary vs replay of GPU records")
+                else:
+                    check_bf16(h, layer, bs[has], repb, res.kept[has_h, 1], "boundary")
+    return g, res
+
+
+def check_bf16(h, layer, slots, rep_f32, ref_f32, what):
+    t = h.wl.state[layer].index_select(0, torch.as_tensor(np.asarray(slots, np.int64),
+                                                          device="cuda"))
+    got_bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    got_bits = got_bits.reshape(rep_f32.shape)
+    assert_bitwise(got_bits, oracle.f32_to_bf16_rne(rep_f32),
+                   f"layer {layer} bf16 {what} vs RNE(replay of GPU records)")
+    got = oracle.bf16_to_f32(got_bits)
+    ref = ref_f32.astype(np.float64)
+    mag = np.abs(ref)
+    ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1e-38))) - 7)
+    slack = TOL * mag.reshape(mag.shape[0], -1).max(1)[:, None, None]
+    assert (np.abs(got - ref) <= ulp + slack).all(), f"layer {layer} bf16 {what}: > 1 ulp"
+
+
+def untouched_slots_equal(state, pre, written):
+    """Every (layer, slot) outside ``written`` (a set of (layer, slot)) is
+    bitwise unchanged."""
+    L, S = state.shape[:2]
+    for layer in range(L):
+        keep = [s for s in range(S) if (layer, s) not in written]
+        idx = torch.as_tensor(keep, device=state.device)
+        a = pool_bits(state[layer].index_select(0, idx))
+        b = pool_bits(pre[layer].index_select(0, idx))
+        assert torch.equal(a, b), f"layer {layer}: a slot outside the write set changed"
+
+
+# --------------------------------------------------------------------------
+
+def test_tiny_every_accepted_count(gdn):
+    """1 layer, 1 sequence, 1 head, D=4; n swept 0..4."""
+    for n in range(5):
+        wl = W.make_workload(W.TINY, device="cuda")
+        h = Harness(wl)
+        pre = wl.state.clone()
+        h.verify_all()
+        torch.cuda.synchronize()
+        assert torch.equal(pool_bits(wl.state), pool_bits(pre)), "verify wrote the checkpoint"
+        h.commit(n=dev_i32([n]))
+        torch.cuda.synchronize()
+        if n == 0:
+            assert torch.equal(pool_bits(wl.state), pool_bits(pre)), "n = 0 changed the state"
+        check_layer(h, 0, [0], [n], pre[0])
+        assert h.err_value() == 0
+
+
+@pytest.mark.parametrize("spec", [W.SINGLE_LAYER, W.ALL_LAYER], ids=lambda s: s.name)
+def test_full_workload(gdn, spec):
+    wl = W.make_workload(spec, device="cuda")
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre))
+    h.commit()
+    torch.cuda.synchronize()
+    rows = np.arange(spec.rows)
+    for layer in range(spec.layers):
+        check_layer(h, layer, rows, wl.n_accept, pre[layer])
+    written = {(l, int(s)) for l in range(spec.layers) for s, n in zip(wl.state_slot, wl.n_accept)
+               if n > 0}
+    untouched_slots_equal(wl.state, pre, written)
+    assert h.err_value() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_mtp_decode_b64_l48(gdn, dtype):
+    """48 layers, batch 64 with 6 graph-padding rows (null slot, zero window),
+    ragged n ~ U{0..4}; every layer and every real row checked."""
+    spec = W.MTP_B64
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre)), "verify wrote the checkpoint"
+    h.commit()
+    torch.cuda.synchronize()
+    real = np.nonzero(wl.state_slot >= 0)[0]
+    pad = np.nonzero(wl.state_slot < 0)[0]
+    assert len(real) == 58 and len(pad) == 6
+    for layer in range(spec.layers):
+        check_layer(h, layer, real, wl.n_accept[real], pre[layer])
+    # padding rows: no output, no record, no state
+    pad_tok = (wl.tok_start[pad][:, None] + np.arange(spec.window)[None]).reshape(-1)
+    assert torch.isnan(h.out[:, torch.as_tensor(pad_tok, device="cuda")]).all()
+    assert torch.isnan(h.rec[:, len(real):]).all()
+    written = {(l, int(s)) for l in range(spec.layers) for s, n in
+               zip(wl.state_slot[real], wl.n_accept[real]) if n > 0}
+    untouched_slots_equal(wl.state, pre, written)
+    assert h.err_value() == 0
+
+
+def ring_run(spec, sample_rows=None, check_all_untouched=True):
+    wl = W.make_workload(spec, device="cuda")
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()                                   # 16 single-token steps per layer
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre)), "verify wrote the checkpoint"
+    outs = [torch.empty(spec.rows, dtype=torch.int32, device="cuda") for _ in range(4)]
+    import gated_deltanet_speculative_gdn_amd as G
+    G.gdn_align_plan(dev_i32(wl.p0), h.n_accept, dev_i32(wl.block_table), spec.block,
+                     spec.rec_tokens, *outs, err_flags=h.err)
+    src, dst, bl, bs = [o.cpu().numpy() for o in outs]
+    want = oracle.align_plan(wl.p0, wl.n_accept, wl.block_table, spec.block, spec.rec_tokens)
+    for got, exp, name in zip((src, dst, bl, bs), want[:4], ("src", "dst", "bnd_len", "bnd_slot")):
+        assert np.array_equal(got, exp), f"align plan {name}"
+    assert not want[4].any()
+    assert np.array_equal(src, wl.state_slot)
+    h.commit(src=outs[0], dst=outs[1], n=h.n_accept, bnd_len=outs[2], bnd_slot=outs[3])
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    rows = np.arange(spec.rows) if sample_rows is None else sample_rows
+    for layer in range(spec.layers):
+        check_layer(h, layer, rows, wl.n_accept[rows], pre[layer], bnd=(bl[rows], bs[rows]),
+                    dst=dst[rows])
+    written = set()
+    for layer in range(spec.layers):
+        for b in range(spec.rows):
+            written.add((layer, int(dst[b])))
+            if bl[b] > 0:
+                written.add((layer, int(bs[b])))
+    if check_all_untouched:
+        untouched_slots_equal(wl.state, pre, written)
+    return wl, (src, dst, bl, bs)
+
+
+def test_ring_align_b256_l36(gdn):
+    """Target-only replay ring: 16 single-token verify steps per layer with the
+    pending records replayed in registers, then one align-mode commit of the
+    16 tokens through the GPU plan (final state and block-boundary state)."""
+    spec = W.RING_ALIGN
+    # sample: every row whose window ends on or crosses a boundary or starts on
+    # one, plus a spread of the others (all rows are checked for plan and write set)
+    wl0 = W.make_workload(W.shrink(spec, layers=1, hv=1, hk=1, num_slots=576), device="cpu")
+    r = wl0.p0 % spec.block
+    special = np.nonzero(np.isin(r, [0, 48, 49, 63]))[0]
+    rest = np.setdiff1d(np.arange(spec.rows), special)[::16]
+    rows = np.union1d(special, rest)
+    wl, plan = ring_run(spec, sample_rows=rows)
+    assert np.array_equal(wl.p0, wl0.p0)
+    bl = plan[2]
+    assert (bl[r == 48] == 0).all() and (bl[r == 0] == 0).all()
+    assert (bl[r == 49] == 15).all() and (bl[r == 63] == 1).all()
+    assert (plan[3][bl > 0] == plan[0][bl > 0]).all(), "boundary state lands in the source slot"
+
+
+def test_align_boundary_in_source_slot_repeated(gdn):
+    """The pages' ordering race (a boundary state written into a source slot
+    another program still reads): 20 runs with fresh random slot placement,
+    every row checked bit-exactly and against the oracle."""
+    for rep in range(20):
+        spec = W.shrink(W.RING_ALIGN, layers=2, rows=32, num_slots=80, hv=4, hk=2,
+                        seed=3000 + rep)
+        ring_run(spec)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_native_snapshots_match_verify_and_commit(gdn, dtype):
+    """The baseline (same arithmetic, every state written) against verify and
+    commit: outputs identical, committed state identical to the native
+    snapshot of the last accepted token, and the native accept copy producing
+    the same pool."""
+    import gated_deltanet_speculative_gdn_amd as G
+    spec = W.shrink(W.ALL_LAYER, layers=3)
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    out_v = h.out.clone()
+    out_n = torch.full_like(h.out, float("nan"))
+    snaps = [torch.empty((spec.rows, spec.hv, spec.rec_tokens, 128, 128), dtype=dtype,
+                         device="cuda") for _ in range(spec.layers)]
+    for layer in range(spec.layers):
+        G.gdn_native_window(h.pools, layer, h.state_slot, h.tok_start, h.win_len, wl.q(layer),
+                            wl.k(layer), wl.v(layer), wl.a[layer], wl.beta[layer], out_n[layer],
+                            snaps[layer], err_flags=h.err)
+    torch.cuda.synchronize()
+    assert torch.equal(out_n.view(torch.int32), out_v.view(torch.int32))
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre))
+    h.commit()
+    committed = wl.state.clone()
+    for layer in range(spec.layers):
+        for b in range(spec.rows):
+            n = int(wl.n_accept[b])
+            if n:
+                got = pool_bits(committed[layer, int(wl.state_slot[b])])
+                assert torch.equal(got, pool_bits(snaps[layer][b, :, n - 1])), (layer, b)
+    wl.state.copy_(pre)
+    G.gdn_native_accept(h.pools, snaps, h.state_slot, h.n_accept, err_flags=h.err)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(committed))
+    assert h.err_value() == 0
+
+
+def test_bf16_verify_is_exact(gdn):
+    """A bf16 checkpoint is widened exactly: verify on it equals, bit for bit,
+    verify on an fp32 pool holding the widened values."""
+    spec = W.shrink(W.ALL_LAYER, layers=2)
+    wl16 = W.make_workload(spec, device="cuda", state_dtype=torch.bfloat16)
+    wl32 = W.make_workload(spec, device="cuda", state_dtype=torch.float32)
+    wl32.state.copy_(wl16.state.float())
+    h16, h32 = Harness(wl16), Harness(wl32)
+    h16.verify_all()
+    h32.verify_all()
+    torch.cuda.synchronize()
+    assert torch.equal(h16.out.view(torch.int32), h32.out.view(torch.int32))
+    assert torch.equal(h16.rec.view(torch.int32), h32.rec.view(torch.int32))
+
+
+def test_onehot_bitwise(gdn):
+    """One-hot q and k, gates exp(0) = 1 or exp(-inf) = 0: single-term
+    reductions, so outputs, records and committed states equal the oracle
+    exactly. A transposed state layout or a wrong key-head map fails here."""
+    spec = W.SINGLE_LAYER
+    wl = W.make_workload(spec, device="cuda", seed=21)
+    rng = np.random.default_rng(21)
+    T, HK = wl.tokens, spec.hk
+    qi = rng.integers(0, 128, size=(T, HK))
+    ki = rng.integers(0, 128, size=(T, HK))
+    q = np.zeros((T, HK, 128), np.float32)
+    k = np.zeros((T, HK, 128), np.float32)
+    q[np.arange(T)[:, None], np.arange(HK)[None], qi] = 1.0
+    k[np.arange(T)[:, None], np.arange(HK)[None], ki] = 1.0
+    wl.qkv[0, :, : HK * 128] = torch.as_tensor(q.reshape(T, -1)).to(torch.bfloat16).cuda()
+    wl.qkv[0, :, HK * 128: 2 * HK * 128] = torch.as_tensor(k.reshape(T, -1)).to(torch.bfloat16).cuda()
+    a = np.where(rng.random((T, spec.hv)) < 0.3, -np.inf, 0.0).astype(np.float32)
+    wl.a[0] = torch.as_tensor(a).cuda()
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    rows = np.arange(spec.rows)
+    g, res = OP.run_layer(wl, 0, rows, keep=wl.n_accept[:, None], state=pre[0])
+    assert np.array_equal(h.outputs(0, rows), res.o)
+    d, kh, gg = h.records(0, rows)
+    assert np.array_equal(d, res.rec_delta) and np.array_equal(kh, res.rec_khat)
+    assert np.array_equal(gg, res.rec_g)
+    assert np.array_equal(h.heads(0, wl.state_slot), res.kept[:, 0])
+
+
+@pytest.mark.parametrize("seed", [31, 32, 33])
+def test_extreme_gates(gdn, seed):
+    """No decay, decay to the subnormal range, full forget; beta 0 and 1."""
+    spec = W.SINGLE_LAYER
+    wl = W.make_workload(spec, device="cuda", seed=seed)
+    rng = np.random.default_rng(seed)
+    T = wl.tokens
+    a = rng.choice(np.array([0.0, -30.0, -100.0, -np.inf, -1e-3], np.float32), size=(T, spec.hv))
+    b = rng.choice(np.array([0.0, 1.0, 0.5, 1e-4], np.float32), size=(T, spec.hv))
+    wl.a[0] = torch.as_tensor(a).cuda()
+    wl.beta[0] = torch.as_tensor(b).cuda()
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    check_layer(h, 0, np.arange(spec.rows), wl.n_accept, pre[0])
+    assert h.err_value() == 0
+
+
+def test_output_scale(gdn):
+    spec = W.shrink(W.SINGLE_LAYER, layers=1)
+    wl = W.make_workload(spec, device="cuda", seed=41)
+    h = Harness(wl)
+    h.verify_all(scale=128 ** -0.5)
+    torch.cuda.synchronize()
+    rows = np.arange(spec.rows)
+    g, res = OP.run_layer(wl, 0, rows, scale=128 ** -0.5)
+    assert_close(h.outputs(0, rows), res.o, 1, "scaled outputs")
+
+
+def test_ragged_windows_strided_output_noncontiguous_rows(gdn):
+    """Windows 4/1/3 on rows whose tokens are not contiguous or in row order,
+    output written through a strided view of a wider buffer, state slots out of
+    order (vLLM RecoverSSM PR, Test Plan: strided views with out=, ragged
+    windows, non-contiguous request rows)."""
+    spec = W.shrink(W.SINGLE_LAYER, rows=3, num_slots=16, slot_mode="random")
+    wl = W.make_workload(spec, device="cuda", seed=51)
+    wl.win_len = np.array([4, 1, 3], np.int32)
+    wl.tok_start = np.array([0, 9, 5], np.int32)
+    wl.n_accept = np.array([3, 1, 2], np.int32)
+    h = Harness(wl)
+    big = torch.full((wl.tokens, spec.hv, 256), float("nan"), device="cuda")
+    out = big[:, :, 64:192]
+    pre = wl.state.clone()
+    h.verify_layer(0, out=out)
+    h.out[0] = out
+    h.commit()
+    torch.cuda.synchronize()
+    check_layer(h, 0, np.arange(3), wl.n_accept, pre[0])
+    assert torch.isnan(big[:, :, :64]).all() and torch.isnan(big[:, :, 192:]).all()
+    covered = {0, 1, 2, 3, 9, 5, 6, 7}
+    for t in range(wl.tokens):
+        if t not in covered:
+            assert torch.isnan(big[t]).all(), t
+    assert h.err_value() == 0
+
+
+def test_device_row_errors_skip_the_row(gdn):
+    spec = W.SINGLE_LAYER
+    wl = W.make_workload(spec, device="cuda", seed=61)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    slot = wl.state_slot.copy()
+    win = wl.win_len.copy()
+    tok = wl.tok_start.copy()
+    slot[0] = spec.num_slots           # slot out of range
+    win[1] = spec.rec_tokens + 1       # window longer than the record capacity
+    tok[2] = wl.tokens - 2             # window runs past the last token
+    h.rec_slot = dev_i32(np.where(np.arange(spec.rows) == 3, 99, wl.rec_slot))
+    h.verify_layer(0, state_slot=dev_i32(slot), win_len=dev_i32(win), tok_start=dev_i32(tok))
+    torch.cuda.synchronize()
+    from gated_deltanet_speculative_gdn_amd import ROW_REC, ROW_SLOT, ROW_WIN, ROW_N, ROW_BND
+    assert h.err_value() == ROW_SLOT | ROW_WIN | ROW_REC
+    for b in range(4):    # skipped rows wrote nothing
+        t0 = wl.tok_start[b]
+        assert torch.isnan(h.out[0, t0:t0 + 4]).all(), b
+    assert torch.isnan(h.rec[0, :3]).all()
+    assert not torch.isnan(h.out[0, wl.tok_start[4]:wl.tok_start[4] + 4]).any()
+    # commit: bad n, bad destination, bad boundary
+    h.err.zero_()
+    h.rec_slot = dev_i32(wl.rec_slot)
+    n = wl.n_accept.copy()
+    n[4] = spec.rec_tokens + 1
+    dst = wl.state_slot.copy()
+    dst[5] = spec.num_slots + 3
+    bl = np.zeros(spec.rows, np.int32)
+    bs = np.full(spec.rows, -1, np.int32)
+    bl[6], bs[6] = n[6], 0             # boundary length must be < n
+    h.commit(n=dev_i32(n), dst=dev_i32(dst), bnd_len=dev_i32(bl), bnd_slot=dev_i32(bs))
+    torch.cuda.synchronize()
+    assert h.err_value() == ROW_N | ROW_SLOT | ROW_BND
+    for b in (4, 5, 6):
+        s = int(wl.state_slot[b])
+        assert torch.equal(wl.state[0, s].view(torch.int32), pre[0, s].view(torch.int32)), b
+
+
+def test_align_plan_matches_oracle(gdn):
+    import gated_deltanet_speculative_gdn_amd as G
+    rows = []
+    for block, T in ((4, 4), (16, 16), (64, 16), (64, 4)):
+        for m in (1, 3):
+            for r in range(block):
+                for n in range(T + 1):
+                    rows.append((block, T, m * block + r, n))
+    for block, T in sorted({(b_, t_) for b_, t_, _, _ in rows}):
+        sel = [(p0, n) for b_, t_, p0, n in rows if (b_, t_) == (block, T)]
+        p0 = np.array([x[0] for x in sel], np.int32)
+        n = np.array([x[1] for x in sel], np.int32)
+        cols = 8
+        table = np.tile((5 * np.arange(cols) + 2).astype(np.int32), (len(sel), 1))
+        table[::7, 1] = -1                                # some unallocated columns
+        outs = [torch.empty(len(sel), dtype=torch.int32, device="cuda") for _ in range(4)]
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        G.gdn_align_plan(dev_i32(p0), dev_i32(n), dev_i32(table), block, T, *outs, err_flags=err)
+        want = oracle.align_plan(p0, n, table, block, T)
+        for got, exp in zip(outs, want[:4]):
+            assert np.array_equal(got.cpu().numpy(), exp)
+        assert int(err.item()) == int(np.bitwise_or.reduce(want[4]))
+    # error rows, one cause each
+    p0 = np.array([0, 10, 10, 3], np.int32)
+    n = np.array([1, 7, 2, 9], np.int32)
+    table = np.tile(np.array([1, 2, -1], np.int32), (4, 1))
+    outs = [torch.empty(4, dtype=torch.int32, device="cuda") for _ in range(4)]
+    for i, (pp, nn, cause) in enumerate(((0, 1, 64), (10, 7, 4), (11, 2, 16), (3, 9, 8))):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        G.gdn_align_plan(dev_i32([pp]), dev_i32([nn]), dev_i32(table[:1]), 4, 6 if cause != 4 else 6,
+                         *[o[:1] for o in outs], err_flags=err)
+        want = oracle.align_plan([pp], [nn], table[:1], 4, 6)
+        assert int(err.item()) == cause == int(want[4][0]), (pp, nn)
+        assert [int(o[0].item()) for o in outs] == [-1, -1, 0, -1]
