@@ -135,8 +135,9 @@ def timed_loop(steps, graph_fn, eager_fn, graph_launches):
         e2.record()
     sync()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    g_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    c_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    # per-launch times: medians over the timed steps (robust to clock transients)
+    g_ms = float(np.median([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    c_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in ev]))
     return wall, g_ms / graph_launches, c_ms, g_ms
 
 
@@ -187,8 +188,8 @@ def counters_traffic(commit_launch_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.MTP_B64.name, choices=sorted(W.WORKLOADS))
     ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--no-native", action="store_true")

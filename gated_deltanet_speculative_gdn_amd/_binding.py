@@ -16,7 +16,7 @@ from .build import LIB_PATH
 
 GDN_MAX_LAYERS = 64
 GDN_HEAD_DIM = 128
-GDN_MAX_REC_TOKENS = 32
+GDN_MAX_REC_TOKENS = 16
 GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
 

@@ -106,7 +106,7 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     int32_t st = check_pools(pools);
     if (st) return st;
     if (layer < 0 || layer >= pools->num_layers || num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads > INT32_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)num_rows * pools->num_v_heads * 4 > INT32_MAX) return GDN_ERR_SHAPE;
     if ((st = check_layer_ptrs(pools, layer, true))) return st;
     if ((st = check_io(io))) return st;
     if (!state_slot || !rec_slot || !tok_start || !win_len) return GDN_ERR_NULL;
@@ -141,7 +141,7 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
     int32_t st = check_pools(pools);
     if (st) return st;
     if (layer < 0 || layer >= pools->num_layers || num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads > INT32_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)num_rows * pools->num_v_heads * 4 > INT32_MAX) return GDN_ERR_SHAPE;
     if ((st = check_layer_ptrs(pools, layer, false))) return st;
     if ((st = check_io(io))) return st;
     if (!state_slot || !tok_start || !win_len || !snap) return GDN_ERR_NULL;
@@ -176,7 +176,7 @@ int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
     int32_t st = check_pools(pools);
     if (st) return st;
     if (num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads * pools->num_layers > INT32_MAX)
+    if ((int64_t)num_rows * pools->num_v_heads * pools->num_layers * 8 > INT32_MAX)
         return GDN_ERR_SHAPE;
     for (int32_t l = 0; l < pools->num_layers; ++l)
         if ((st = check_layer_ptrs(pools, l, true))) return st;

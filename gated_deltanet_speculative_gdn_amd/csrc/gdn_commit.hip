@@ -17,7 +17,10 @@
 // t + 256*i, so each load instruction of the workgroup covers 4 KiB of
 // contiguous memory -- stages the n records in LDS, replays n tokens
 // elementwise (no reductions), then stores the final state and, in align mode,
-// the boundary state kept in a second register tile. Because every thread
+// the boundary state kept in a second register tile. State loads and stores
+// are nontemporal (streamed past the caches: nothing here is reused), and the
+// workgroup ids are remapped so that each XCD streams a contiguous range of
+// heads. Because every thread
 // reads all of its source elements before its first store and writes only the
 // elements it read, a destination or boundary slot equal to the source slot is
 // safe; the pages' read-after-overwrite race between programs cannot occur.
@@ -29,70 +32,83 @@
 namespace gdn {
 namespace {
 
-// Ownership of the elements of one head by thread t:
-//   fp32: 16 pieces of 4 floats, piece f = t + 256*i: row f/32, columns 4*(f%32)..+3.
-//   bf16: 8 pieces of 8 values, piece f = t + 256*i: row f/16, columns 8*(f%16)..+7.
-template <typename StateT> struct HeadIO;
+// Ownership of the elements of one head. The head is cut into 16-byte pieces
+// (fp32: 4096 pieces of 4 values, piece f = row f/32, columns 4*(f%32)..+3;
+// bf16: 2048 pieces of 8 values, piece f = row f/16, columns 8*(f%16)..+7) and
+// split over SPLIT workgroups: workgroup `part` owns a contiguous run of
+// 128/SPLIT rows, and its thread t owns pieces base + t + 256*i. Each load or
+// store instruction of a workgroup therefore covers 4 KiB of contiguous memory.
+template <typename StateT, int SPLIT> struct HeadIO;
 
-template <> struct HeadIO<float> {
-    static constexpr int kPieces = 16;
-    typedef f32x4 Raw;
-    __device__ static void load(const float* head, int t, f32x4 (&h)[16]) {
+template <int SPLIT> struct HeadIO<float, SPLIT> {
+    static constexpr int kPer = 16 / SPLIT;              // pieces (f32x4) per thread
+    __device__ static int piece(int part, int t, int i) { return part * (4096 / SPLIT) + t + kThreads * i; }
+    template <bool NT>
+    __device__ static void load(const float* head, int part, int t, f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) h[i] = ld4(head + 4 * (t + kThreads * i));
+        for (int i = 0; i < kPer; ++i)
+            h[i] = NT ? ld4_nt(head + 4 * piece(part, t, i)) : ld4(head + 4 * piece(part, t, i));
     }
     template <bool NT>
-    __device__ static void store(float* head, int t, const f32x4 (&h)[16]) {
+    __device__ static void store(float* head, int part, int t, const f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if constexpr (NT) st4_nt(head + 4 * (t + kThreads * i), h[i]);
-            else st4(head + 4 * (t + kThreads * i), h[i]);
+        for (int i = 0; i < kPer; ++i) {
+            if constexpr (NT) st4_nt(head + 4 * piece(part, t, i), h[i]);
+            else st4(head + 4 * piece(part, t, i), h[i]);
         }
     }
-    // row of element e of piece i, and the column of element 0
-    __device__ static int row(int t, int i) { return (t + kThreads * i) >> 5; }
+    // row of piece i relative to the workgroup's first row
+    __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 5; }
     __device__ static int col0(int t) { return 4 * (t & 31); }
 };
 
-template <> struct HeadIO<uint16_t> {
-    static constexpr int kPieces = 8;
-    // the same 64 values per thread, held as 16 f32x4: h[2i] = columns +0..3, h[2i+1] = +4..7
-    __device__ static void load(const uint16_t* head, int t, f32x4 (&h)[16]) {
+template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
+    static constexpr int kPieces = 8 / SPLIT;            // 16-byte pieces per thread
+    static constexpr int kPer = 2 * kPieces;             // held as f32x4 halves
+    __device__ static int piece(int part, int t, int i) { return part * (2048 / SPLIT) + t + kThreads * i; }
+    template <bool NT>
+    __device__ static void load(const uint16_t* head, int part, int t, f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(head + 8 * (t + kThreads * i));
+        for (int i = 0; i < kPieces; ++i) {
+            const u32x4* q = reinterpret_cast<const u32x4*>(head + 8 * piece(part, t, i));
+            const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
             h[2 * i] = f32x4{bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
             h[2 * i + 1] = f32x4{bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
         }
     }
     template <bool NT>
-    __device__ static void store(uint16_t* head, int t, const f32x4 (&h)[16]) {
+    __device__ static void store(uint16_t* head, int part, int t, const f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kPieces; ++i) {
             const f32x4 a = h[2 * i], c = h[2 * i + 1];
             const u32x4 x{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y),
                           pack_bf16(c.z, c.w)};
-            u32x4* dst = reinterpret_cast<u32x4*>(head + 8 * (t + kThreads * i));
+            u32x4* dst = reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i));
             if constexpr (NT) __builtin_nontemporal_store(x, dst);
             else *dst = x;
         }
     }
-    __device__ static int row(int t, int i) { return (t + kThreads * i) >> 4; }
+    __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 4; }
     __device__ static int col0(int t) { return 8 * (t & 15); }
 };
 
-template <typename StateT, bool ALIGN>
+template <typename StateT, bool ALIGN, int SPLIT, bool NT>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
+    typedef HeadIO<StateT, SPLIT> IO;
+    constexpr int kRows = kDim / SPLIT;   // rows of the head this workgroup owns
     extern __shared__ float lds[];
     const int T = p.T;
-    float* d_l = lds;                 // [n][128] corrections
+    float* d_l = lds;                 // [n][kRows] corrections of the owned rows
     float* k_l = lds + T * kDim;      // [n][128] normalised keys
     float* g_l = lds + 2 * T * kDim;  // [n] decays
 
-    const int64_t wg = blockIdx.x;
-    const int hv = (int)(wg % p.hv);
-    const int64_t lb = wg / p.hv;
+    // logical id: (layer, row, value head, part), XCD-contiguous
+    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int part = (int)(wg % SPLIT);
+    const int64_t head_id = wg / SPLIT;
+    const int hv = (int)(head_id % p.hv);
+    const int64_t lb = head_id / p.hv;
     const int b = (int)(lb % p.num_rows);
     const int layer = (int)(lb / p.num_rows);
 
@@ -114,36 +130,40 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     if (rs < 0 || rs >= p.num_rec_slots) err |= kRowRec;
     if (ALIGN && bl != 0 && (bl < 0 || bl >= n || bs < 0 || bs >= p.num_slots)) err |= kRowBnd;
     if (err) {
-        if (threadIdx.x == 0 && hv == 0 && layer == 0 && p.err) atomicOr(p.err, err);
+        if (threadIdx.x == 0 && hv == 0 && layer == 0 && part == 0 && p.err) atomicOr(p.err, err);
         return;
     }
     const bool write_bnd = ALIGN && bl > 0 && bs != dst;
 
     const int t = threadIdx.x;
     StateT* pool = static_cast<StateT*>(p.state[layer]);
-    const int64_t head_off = (int64_t)p.hv * kHeadElems;
-    f32x4 h[16];
-    HeadIO<StateT>::load(pool + src * head_off + (int64_t)hv * kHeadElems, t, h);
+    const int64_t slot_elems = (int64_t)p.hv * kHeadElems;
+    const int64_t head_off = (int64_t)hv * kHeadElems;
+    f32x4 h[IO::kPer];
+    IO::template load<NT>(pool + src * slot_elems + head_off, part, t, h);
 
-    // ---- the n records into LDS ----
+    // ---- the n records into LDS (own rows of the corrections, all of the keys) ----
     const float* recb = p.rec[layer] + ((int64_t)rs * p.hv + hv) * p.rec_stride;
-    for (int i = t; i < n * (kDim / 4); i += kThreads) {
-        st4(d_l + 4 * i, ld4(recb + 4 * i));
-        st4(k_l + 4 * i, ld4(recb + (int64_t)T * kDim + 4 * i));
+    constexpr int kRow4 = kRows / 4;
+    for (int i = t; i < n * kRow4; i += kThreads) {
+        const int tt = i / kRow4;
+        st4(d_l + 4 * i, ld4(recb + tt * kDim + part * kRows + 4 * (i - tt * kRow4)));
     }
+    for (int i = t; i < n * (kDim / 4); i += kThreads)
+        st4(k_l + 4 * i, ld4(recb + (int64_t)T * kDim + 4 * i));
     if (t < n) g_l[t] = recb[2 * (int64_t)T * kDim + t];
     __syncthreads();
 
     // ---- replay: h = fma(delta_t[row], k_hat_t[col], h * g_t) ----
-    f32x4 hb[ALIGN ? 16 : 1];
-    const int c0 = HeadIO<StateT>::col0(t);
+    f32x4 hb[ALIGN ? IO::kPer : 1];
+    const int c0 = IO::col0(t);
     for (int tt = 0; tt < n; ++tt) {
         const float g = g_l[tt];
         if constexpr (sizeof(StateT) == 4) {
             const f32x4 kh = ld4(k_l + tt * kDim + c0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float d = d_l[tt * kDim + HeadIO<StateT>::row(t, i)];
+            for (int i = 0; i < IO::kPer; ++i) {
+                const float d = d_l[tt * kRows + IO::local_row(t, i)];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * g);
             }
@@ -151,8 +171,8 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
             const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
             const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float d = d_l[tt * kDim + HeadIO<StateT>::row(t, i)];
+            for (int i = 0; i < IO::kPer / 2; ++i) {
+                const float d = d_l[tt * kRows + IO::local_row(t, i)];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * g);
@@ -163,17 +183,15 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         if constexpr (ALIGN) {
             if (tt + 1 == bl) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) hb[i] = h[i];
+                for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
             }
         }
     }
 
     // ---- final state first, then the boundary state ----
-    HeadIO<StateT>::template store<true>(pool + dst * head_off + (int64_t)hv * kHeadElems, t, h);
+    IO::template store<NT>(pool + dst * slot_elems + head_off, part, t, h);
     if constexpr (ALIGN) {
-        if (write_bnd)
-            HeadIO<StateT>::template store<true>(pool + bs * head_off + (int64_t)hv * kHeadElems,
-                                                 t, hb);
+        if (write_bnd) IO::template store<NT>(pool + bs * slot_elems + head_off, part, t, hb);
     }
 }
 
@@ -209,14 +227,37 @@ __global__ void __launch_bounds__(kThreads) accept_kernel(AcceptParams p)
     for (int i = 0; i < kPer; ++i) __builtin_nontemporal_store(x[i], o4 + threadIdx.x + kThreads * i);
 }
 
-template <typename StateT, bool ALIGN>
+template <typename StateT, bool ALIGN, int SPLIT, bool NT>
 hipError_t launch_c(const CommitParams& p, hipStream_t s)
 {
     CommitParams args = p;
     void* kargs[] = {&args};
-    const uint64_t grid = (uint64_t)p.num_layers * p.num_rows * p.hv;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN>),
+    const uint64_t grid = (uint64_t)p.num_layers * p.num_rows * p.hv * SPLIT;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT>),
                            dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
+}
+
+template <bool ALIGN, int SPLIT, bool NT>
+hipError_t launch_c_dtype(const CommitParams& p, bool bf16_state, hipStream_t s)
+{
+    return bf16_state ? launch_c<uint16_t, ALIGN, SPLIT, NT>(p, s)
+                      : launch_c<float, ALIGN, SPLIT, NT>(p, s);
+}
+
+template <bool ALIGN>
+hipError_t launch_c_shape(const CommitParams& p, bool bf16_state, int split, bool nt, hipStream_t s)
+{
+    switch (split * 2 + (nt ? 1 : 0)) {
+    case 2: return launch_c_dtype<ALIGN, 1, false>(p, bf16_state, s);
+    case 3: return launch_c_dtype<ALIGN, 1, true>(p, bf16_state, s);
+    case 4: return launch_c_dtype<ALIGN, 2, false>(p, bf16_state, s);
+    case 5: return launch_c_dtype<ALIGN, 2, true>(p, bf16_state, s);
+    case 8: return launch_c_dtype<ALIGN, 4, false>(p, bf16_state, s);
+    case 9: return launch_c_dtype<ALIGN, 4, true>(p, bf16_state, s);
+    case 16: return launch_c_dtype<ALIGN, 8, false>(p, bf16_state, s);
+    case 17: return launch_c_dtype<ALIGN, 8, true>(p, bf16_state, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename StateT>
@@ -231,10 +272,16 @@ hipError_t launch_a(const AcceptParams& p, hipStream_t s)
 
 }  // namespace
 
+hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool align, int split,
+                               bool nontemporal, hipStream_t s)
+{
+    return align ? launch_c_shape<true>(p, bf16_state, split, nontemporal, s)
+                 : launch_c_shape<false>(p, bf16_state, split, nontemporal, s);
+}
+
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s)
 {
-    if (bf16_state) return align ? launch_c<uint16_t, true>(p, s) : launch_c<uint16_t, false>(p, s);
-    return align ? launch_c<float, true>(p, s) : launch_c<float, false>(p, s);
+    return launch_commit_shape(p, bf16_state, align, kCommitSplit, kCommitNontemporal, s);
 }
 
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s)

@@ -74,5 +74,19 @@ __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4
 __device__ __forceinline__ void st4_nt(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
+__device__ __forceinline__ f32x4 ld4_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
+// The dispatcher hands workgroup w to XCD w % 8 (eight XCDs, each with its
+// own L2). Remapping w so that the workgroups one XCD receives take one
+// contiguous range of logical ids lets each XCD stream a contiguous stretch of
+// memory instead of every eighth piece. A bijection on [0, grid); the tail
+// past the last multiple of 8 keeps its id.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int64_t xcd_contiguous_id(int64_t w, int64_t grid) {
+    const int64_t per = grid / kNumXcd;
+    return w < per * kNumXcd ? (w % kNumXcd) * per + w / kNumXcd : w;
+}
 
 }  // namespace gdn

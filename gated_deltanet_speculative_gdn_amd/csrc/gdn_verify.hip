@@ -5,25 +5,38 @@
 // short conv", Purpose (verify runs the draft window from the checkpoint,
 // writes the per-token outputs and an fp32 record of correction, normalised key
 // and gate, never the state) and Test Result (the record holds the decay that
-// was multiplied in); the rule itself is the gated delta rule of "Gated Delta
-// Networks" (Yang, Kautz, Hatamizadeh, ICLR 2025). Ring mode (records of
-// earlier single-token steps replayed in registers before the window) follows
-// the 16-token replay buffer of lmdeploy PR #5028 (Performance test settings).
+// was multiplied in; the commit's forward replay of it equals the native
+// per-token state bit for bit); the rule itself is the gated delta rule of
+// "Gated Delta Networks" (Yang, Kautz, Hatamizadeh, ICLR 2025). Ring mode
+// (records of earlier single-token steps applied before the window) follows the
+// 16-token replay buffer of lmdeploy PR #5028 (Performance test settings).
 //
-// One workgroup of four wave64s per (row, value head). The 128x128 fp32 head
-// lives in registers, 64 values per lane: lane l holds rows 4*(l/8) + r and
-// columns 4*(l%8) + 32*c + e (r, c, e = 0..3), so each of its 16 vector loads
-// reads one 16-byte piece and eight neighbouring lanes read a whole 128-byte
-// row segment. The two length-128 reductions per token (h'k_hat and h q_tilde)
-// are 16 fmas in the lane followed by a three-step DPP sum over the eight lanes
-// of a row group -- no LDS traffic and no barrier inside the token loop. The
-// window's normalised q, k, the values, gates and ring records are staged in
-// LDS once, before the loop.
+// Verify never writes the state, so it never forms S_t. With the positions
+// 0..P-1 of a row (0..j0-1: pending ring records, j0..P-1: the window), the
+// decay products G(a, b) = g_a * ... * g_{b-1} and the checkpoint S0, the rule
+// S_{p+1} = g_p S_p + delta_p k_p^T unrolls to
+//   u_p = G(0,p+1) (S0 k_p) + sum_{j<p}  G(j+1,p+1) (k_j . k_p) delta_j
+//   o_p = G(0,p+1) (S0 q_p) + sum_{j<=p} G(j+1,p+1) (k_j . q_p) delta_j
+//   delta_p = beta_p (v_p - u_p)
+// (k, q normalised; q scaled). The only work proportional to the 128x128 head
+// is the contraction of S0 with the 2w window vectors: 2w fmas per state
+// element instead of the per-token rule's 4w operations, and ring records cost
+// a scalar term each instead of a pass over the head. The 2w-column product is
+// a dense contraction, but at w = 4 it would fill half of an fp32 16x16x4 MFMA
+// and run at the vector-fma rate, so it stays on the vector ALU.
 //
-// The native baseline is the same template with SNAP = true: identical
-// arithmetic, plus a store of the state after every token. Verify outputs and
-// records are therefore bit-identical to the baseline's, and the commit's
-// replay of them reproduces the baseline's states bit for bit.
+// One workgroup of four wave64s per (row, value head, chunk of 32*R head rows);
+// workgroup ids are remapped so that each XCD streams a contiguous stretch of
+// the pool. Lane l holds head rows R*(l/8) + r and columns 4*(l%8) + 32*c + e
+// (c, e = 0..3): each 16-byte load of eight neighbouring lanes covers a whole
+// 128-byte row segment, and a length-128 reduction is 16 fmas in the lane plus
+// a three-step DPP sum over the eight lanes of a row group. The window's
+// vectors and the per-item scalar coefficients are staged in LDS once.
+//
+// The native baseline is the same template with SNAP = true: the same
+// corrections and outputs, bit for bit, then the states S_1..S_w materialised
+// with the commit's update h = fma(delta, k, h * g) and written out -- so the
+// commit's replay of verify's records reproduces the baseline's states exactly.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
@@ -32,63 +45,108 @@
 namespace gdn {
 namespace {
 
-// Register tile: h[r][c] holds row 4*grp + r, columns 4*lane8 + 32*c .. +3.
-template <typename StateT> struct TileIO;
+// ---- register tile of R rows: h[r][c] = row row0 + R*grp + r, columns 4*lane8 + 32*c .. +3
+template <typename StateT, int R> struct TileIO;
 
-template <> struct TileIO<float> {
-    __device__ static void load(const float* head, int grp, int lane8, f32x4 (&h)[4][4]) {
+template <int R> struct TileIO<float, R> {
+    __device__ static void load(const float* head, int row0, int grp, int lane8, f32x4 (&h)[R][4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                h[r][c] = ld4(head + (4 * grp + r) * kDim + 4 * lane8 + 32 * c);
+                h[r][c] = ld4_nt(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c);
     }
-    __device__ static void store(float* head, int grp, int lane8, const f32x4 (&h)[4][4]) {
+    __device__ static void store(float* head, int row0, int grp, int lane8, const f32x4 (&h)[R][4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                st4(head + (4 * grp + r) * kDim + 4 * lane8 + 32 * c, h[r][c]);
+                st4_nt(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c, h[r][c]);
     }
 };
 
-// bf16 pool: the same element ownership, 8-byte loads (four bf16 values).
-template <> struct TileIO<uint16_t> {
-    __device__ static void load(const uint16_t* head, int grp, int lane8, f32x4 (&h)[4][4]) {
+// bf16 pool: the same element ownership, 8-byte pieces (four bf16 values).
+template <int R> struct TileIO<uint16_t, R> {
+    __device__ static void load(const uint16_t* head, int row0, int grp, int lane8,
+                                f32x4 (&h)[R][4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const u32x2 x = *reinterpret_cast<const u32x2*>(
-                    head + (4 * grp + r) * kDim + 4 * lane8 + 32 * c);
+                const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+                    head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c));
                 h[r][c] = f32x4{bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
             }
     }
-    __device__ static void store(uint16_t* head, int grp, int lane8, const f32x4 (&h)[4][4]) {
+    __device__ static void store(uint16_t* head, int row0, int grp, int lane8,
+                                 const f32x4 (&h)[R][4]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const f32x4 v = h[r][c];
-                *reinterpret_cast<u32x2*>(head + (4 * grp + r) * kDim + 4 * lane8 + 32 * c) =
-                    u32x2{pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)};
+                __builtin_nontemporal_store(
+                    u32x2{pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)},
+                    reinterpret_cast<u32x2*>(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c));
             }
     }
 };
 
-template <typename StateT, bool SNAP>
+// Row-group dot product of the tile with one staged 128-vector: R sums, each
+// identical in all eight lanes of the group.
+template <int R>
+__device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x, int lane8, float (&out)[R])
+{
+    f32x4 xv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xv[c] = ld4(x + 4 * lane8 + 32 * c);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(h[r][c][e], xv[c][e], acc);
+        out[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) out[r] = sum8(out[r]);
+}
+
+// LDS layout of one workgroup (floats), T = record capacity:
+//   khat [T][128]  normalised keys of every position (ring records and window)
+//   vd   [T][128]  ring positions: recorded corrections; window positions: values
+//   qt   [T][128]  window positions: normalised, scaled queries
+//   dw   [T][128]  window positions: the corrections computed here
+//   g [T], be [T], g0 [T] = G(0, p+1)
+//   ca [T][T] = G(j+1, p+1) (k_j . k_p), j < p;  cb [T][T] = G(j+1, p+1) (k_j . q_p), j <= p
+struct Lds {
+    float *khat, *vd, *qt, *dw, *g, *be, *g0, *ca, *cb;
+    __device__ Lds(float* base, int T)
+        : khat(base), vd(base + T * kDim), qt(base + 2 * T * kDim), dw(base + 3 * T * kDim),
+          g(base + 4 * T * kDim), be(g + T), g0(be + T), ca(g0 + T), cb(ca + T * T) {}
+};
+
+// R = rows of the head per thread; a workgroup covers 32*R rows, so a head is
+// split over 4/R workgroups. Each stages the whole window (the norms and dot
+// products need all 128 columns); the head-level record fields (key, gate) are
+// written by the first chunk.
+template <typename StateT, bool SNAP, int R>
 __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
 {
-    extern __shared__ float lds[];
+    static_assert(R == 1 || R == 2 || R == 4, "rows per thread");
+    constexpr int kChunks = kDim / (32 * R);
+    extern __shared__ float lds_raw[];
     const int T = p.T;
-    float* khat_l = lds;                  // [T][128] normalised keys (ring and window)
-    float* vd_l = lds + T * kDim;         // [T][128] ring: corrections; window: values
-    float* qt_l = lds + 2 * T * kDim;     // [T][128] normalised, scaled queries
-    float* g_l = lds + 3 * T * kDim;      // [T] decays
-    float* be_l = g_l + T;                // [T] write strengths
+    const Lds L(lds_raw, T);
 
-    const int b = blockIdx.x / p.hv;
-    const int hv = blockIdx.x - b * p.hv;
+    const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int chunk = (int)(item % kChunks);
+    const int64_t bh = item / kChunks;
+    const int b = (int)(bh / p.hv);
+    const int hv = (int)(bh - (int64_t)b * p.hv);
+    const int row0 = chunk * 32 * R;
+    const bool lead = chunk == 0;
 
     // ---- row decode: a null slot or an empty window is padding ----
     const int slot = p.state_slot[b];
@@ -109,45 +167,79 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         if (threadIdx.x == 0 && p.err) atomicOr(p.err, err);
         return;
     }
+    const int P = j0 + w;
 
     const int tid = threadIdx.x;
     const int lane8 = tid & 7;
     const int grp = tid >> 3;
-
-    // ---- checkpoint head into registers (issued first, consumed after the barrier) ----
-    const StateT* head = static_cast<const StateT*>(p.state) + ((int64_t)slot * p.hv + hv) * kHeadElems;
-    f32x4 h[4][4];
-    TileIO<StateT>::load(head, grp, lane8, h);
-
-    float* recb = nullptr;
-    if constexpr (!SNAP) {
-        recb = p.rec + ((int64_t)rs * p.hv + hv) * p.rec_stride;
-        // pending ring records (positions 0 .. j0-1) into LDS
-        for (int i = tid; i < j0 * (kDim / 4); i += kThreads) {
-            st4(vd_l + 4 * i, ld4(recb + 4 * i));
-            st4(khat_l + 4 * i, ld4(recb + (int64_t)T * kDim + 4 * i));
-        }
-        for (int i = tid; i < j0; i += kThreads) g_l[i] = recb[2 * (int64_t)T * kDim + i];
-    }
-
-    // ---- window vectors: three jobs per token (q, k, v), one 16-lane DPP row each ----
     const int lane16 = tid & 15;
+
+    // ---- issue the window's loads first, then the checkpoint tile: loads
+    // complete in issue order, so the staging below waits only for the small
+    // window data and overlaps the tile's transfer ----
     const int hk = hv / p.group;
-    for (int jb = tid >> 4; jb < 3 * w; jb += kThreads / 16) {
+    // uniform base pointers of the window's first token; a lane's job picks one
+    const uint16_t* q_base = p.q + (int64_t)ts * p.q_ts + (int64_t)hk * p.q_hs;
+    const uint16_t* k_base = p.k + (int64_t)ts * p.k_ts + (int64_t)hk * p.k_hs;
+    const uint16_t* v_base = p.v + (int64_t)ts * p.v_ts + (int64_t)hv * p.v_hs;
+    auto job_src = [&](int jb) -> const uint16_t* {
         const int t = jb / 3;
         const int kind = jb - 3 * t;
-        const int64_t tok = (int64_t)ts + t;
-        const int pos = j0 + t;
-        const uint16_t* src = kind == 0 ? p.q + tok * p.q_ts + hk * p.q_hs
-                            : kind == 1 ? p.k + tok * p.k_ts + hk * p.k_hs
-                                        : p.v + tok * p.v_ts + hv * p.v_hs;
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 8 * lane16);
+        const uint16_t* cq = q_base + t * p.q_ts;     // select among addresses, not among
+        const uint16_t* ck = k_base + t * p.k_ts;     // argument fields (which would be a
+        const uint16_t* cv = v_base + t * p.v_ts;     // per-lane load of the argument block)
+        return kind == 0 ? cq : kind == 1 ? ck : cv;
+    };
+    const int jb0 = tid >> 4;                       // this lane's first (q, k, v) job
+    u32x4 raw0 = {0u, 0u, 0u, 0u};
+    if (jb0 < 3 * w) raw0 = *reinterpret_cast<const u32x4*>(job_src(jb0) + 8 * lane16);
+    // gate inputs of token min(tid, w-1): unconditional, so no use of them is
+    // hoisted above the tile loads below
+    const int64_t gtok = (int64_t)ts + (tid < w ? tid : w - 1);
+    const float a_in = p.a_log[gtok * p.g_ts + hv];
+    const float b_in = p.beta[gtok * p.g_ts + hv];
+    float* recb = nullptr;
+    f32x4 ring_d[2], ring_k[2];
+    float ring_g = 0.f;
+    if constexpr (!SNAP) {
+        recb = p.rec + ((int64_t)rs * p.hv + hv) * p.rec_stride;
+        // pending ring records (positions 0 .. j0-1): at most 2 pieces per thread (T <= 16)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int i = tid + q * kThreads;
+            if (i < j0 * (kDim / 4)) {
+                ring_d[q] = ld4(recb + 4 * i);
+                ring_k[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
+            }
+        }
+        if (tid < j0) ring_g = recb[2 * (int64_t)T * kDim + tid];
+    }
+    const StateT* head = static_cast<const StateT*>(p.state) + ((int64_t)slot * p.hv + hv) * kHeadElems;
+    f32x4 h[R][4];
+    TileIO<StateT, R>::load(head, row0, grp, lane8, h);
+
+    // ---- stage the window in LDS ----
+    if constexpr (!SNAP) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int i = tid + q * kThreads;
+            if (i < j0 * (kDim / 4)) {
+                st4(L.vd + 4 * i, ring_d[q]);
+                st4(L.khat + 4 * i, ring_k[q]);
+            }
+        }
+        if (tid < j0) L.g[tid] = ring_g;
+    }
+    for (int jb = jb0; jb < 3 * w; jb += kThreads / 16) {
+        const int t = jb / 3;
+        const int kind = jb - 3 * t;
+        const u32x4 raw = jb == jb0 ? raw0 : *reinterpret_cast<const u32x4*>(job_src(jb) + 8 * lane16);
         float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-        const int off = pos * kDim + 8 * lane16;
+        const int off = (j0 + t) * kDim + 8 * lane16;
         if (kind == 2) {
-            st4(vd_l + off, f32x4{x[0], x[1], x[2], x[3]});
-            st4(vd_l + off + 4, f32x4{x[4], x[5], x[6], x[7]});
+            st4(L.vd + off, f32x4{x[0], x[1], x[2], x[3]});
+            st4(L.vd + off + 4, f32x4{x[4], x[5], x[6], x[7]});
             continue;
         }
         float ssq = 0.f;
@@ -160,12 +252,12 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         if (kind == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = x[i] * p.scale;
-            st4(qt_l + off, f32x4{x[0], x[1], x[2], x[3]});
-            st4(qt_l + off + 4, f32x4{x[4], x[5], x[6], x[7]});
+            st4(L.qt + off, f32x4{x[0], x[1], x[2], x[3]});
+            st4(L.qt + off + 4, f32x4{x[4], x[5], x[6], x[7]});
         } else {
-            st4(khat_l + off, f32x4{x[0], x[1], x[2], x[3]});
-            st4(khat_l + off + 4, f32x4{x[4], x[5], x[6], x[7]});
-            if constexpr (!SNAP) {
+            st4(L.khat + off, f32x4{x[0], x[1], x[2], x[3]});
+            st4(L.khat + off + 4, f32x4{x[4], x[5], x[6], x[7]});
+            if (!SNAP && lead) {
                 float* rk = recb + (int64_t)T * kDim + off;
                 st4(rk, f32x4{x[0], x[1], x[2], x[3]});
                 st4(rk + 4, f32x4{x[4], x[5], x[6], x[7]});
@@ -173,118 +265,158 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         }
     }
     for (int t = tid; t < w; t += kThreads) {
-        const int64_t tok = (int64_t)ts + t;
-        const float g = expf(p.a_log[tok * p.g_ts + hv]);
-        g_l[j0 + t] = g;
-        be_l[j0 + t] = p.beta[tok * p.g_ts + hv];
-        if constexpr (!SNAP) recb[2 * (int64_t)T * kDim + j0 + t] = g;
+        float av = a_in, bv = b_in;
+        if (t != tid) {          // windows longer than the workgroup (not reachable at T <= 16)
+            const int64_t tok = (int64_t)ts + t;
+            av = p.a_log[tok * p.g_ts + hv];
+            bv = p.beta[tok * p.g_ts + hv];
+        }
+        const float g = expf(av);
+        L.g[j0 + t] = g;
+        L.be[j0 + t] = bv;
+        if (!SNAP && lead) recb[2 * (int64_t)T * kDim + j0 + t] = g;
     }
     __syncthreads();
 
-    // ---- ring: replay the pending records onto the checkpoint ----
-    for (int pos = 0; pos < j0; ++pos) {
-        const float g = g_l[pos];
-        f32x4 kh[4];
+    // ---- per-item scalars: G(0, p+1) and the coefficients of earlier corrections ----
+    // Window position p has 2p + 1 dot-product jobs: (k_j . k_p) for j < p, then
+    // (k_j . q_p) for j <= p; jobs of p start at p^2 - j0^2.
+    const int njobs = P * P - j0 * j0;
+    for (int jb = tid >> 4; jb < njobs; jb += kThreads / 16) {
+        int pp = j0;
+        while ((pp + 1) * (pp + 1) - j0 * j0 <= jb) ++pp;
+        const int rem = jb - (pp * pp - j0 * j0);
+        const bool is_q = rem >= pp;
+        const int j = is_q ? rem - pp : rem;
+        const float* a = L.khat + j * kDim + 8 * lane16;
+        const float* c = (is_q ? L.qt : L.khat) + pp * kDim + 8 * lane16;
+        const f32x4 a0 = ld4(a), a1 = ld4(a + 4), c0 = ld4(c), c1 = ld4(c + 4);
+        float dot = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kh[c] = ld4(khat_l + pos * kDim + 4 * lane8 + 32 * c);
-        const f32x4 d = ld4(vd_l + pos * kDim + 4 * grp);
+        for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a0[e], c0[e], dot);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a1[e], c1[e], dot);
+        dot = sum16(dot);
+        float gam = 1.f;
+        for (int m = j + 1; m <= pp; ++m) gam = gam * L.g[m];
+        if (lane16 == 0) (is_q ? L.cb : L.ca)[j * T + pp] = gam * dot;
+    }
+    for (int t = tid; t < w; t += kThreads) {
+        float gam = 1.f;
+        for (int m = 0; m <= j0 + t; ++m) gam = gam * L.g[m];
+        L.g0[j0 + t] = gam;
+    }
+    __syncthreads();
+
+    // ---- the window, position by position ----
+    const int rbase = row0 + R * grp;
+    for (int pp = j0; pp < P; ++pp) {
+        const float g0 = L.g0[pp];
+        float pk[R];
+        tile_dot<R>(h, L.khat + pp * kDim, lane8, pk);
+        float u[R];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+        for (int r = 0; r < R; ++r) u[r] = g0 * pk[r];
+        for (int j = 0; j < pp; ++j) {
+            const float cf = L.ca[j * T + pp];
+            const float* dj = (j < j0 ? L.vd : L.dw) + j * kDim + rbase;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[r][c][e] = __builtin_fmaf(d[r], kh[c][e], h[r][c][e] * g);
+            for (int r = 0; r < R; ++r) u[r] = __builtin_fmaf(cf, dj[r], u[r]);
+        }
+        const float be = L.be[pp];
+        float d[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) d[r] = be * (L.vd[pp * kDim + rbase + r] - u[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) L.dw[pp * kDim + rbase + r] = d[r];   // same value in all 8 lanes
+
+        float pq[R];
+        tile_dot<R>(h, L.qt + pp * kDim, lane8, pq);
+        float o[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) o[r] = g0 * pq[r];
+        for (int j = 0; j < pp; ++j) {
+            const float cf = L.cb[j * T + pp];
+            const float* dj = (j < j0 ? L.vd : L.dw) + j * kDim + rbase;
+#pragma unroll
+            for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cf, dj[r], o[r]);
+        }
+        const float cpp = L.cb[pp * T + pp];
+#pragma unroll
+        for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cpp, d[r], o[r]);
+
+        // lane r of the row group stores row r
+        float* orow = p.out + ((int64_t)ts + (pp - j0)) * p.o_ts + hv * p.o_hs + rbase;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (lane8 == r) {
+                orow[r] = o[r];
+                if constexpr (!SNAP) recb[pp * kDim + rbase + r] = d[r];
+            }
+        }
     }
 
-    // ---- the window, token by token ----
-    for (int t = 0; t < w; ++t) {
-        const int pos = j0 + t;
-        const float g = g_l[pos];
-        const float be = be_l[pos];
-        f32x4 kh[4];
+    // ---- native baseline: materialise and write S_1..S_w ----
+    if constexpr (SNAP) {
+        for (int t = 0; t < w; ++t) {
+            const float g = L.g[t];
+            f32x4 kh[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kh[c] = ld4(khat_l + pos * kDim + 4 * lane8 + 32 * c);
-        const f32x4 vv = ld4(vd_l + pos * kDim + 4 * grp);
-
-        // h' = g h, u = h' k_hat
-        float u[4];
+            for (int c = 0; c < 4; ++c) kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float acc = 0.f;
+            for (int r = 0; r < R; ++r) {
+                const float d = L.dw[t * kDim + rbase + r];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    h[r][c][e] = h[r][c][e] * g;
-                    acc = __builtin_fmaf(h[r][c][e], kh[c][e], acc);
-                }
-            u[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = sum8(u[r]);
-
-        // delta = beta (v - u);  h = fma(delta, k_hat, h')
-        f32x4 d;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = be * (vv[r] - u[r]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    h[r][c][e] = __builtin_fmaf(d[r], kh[c][e], h[r][c][e]);
-
-        // o = h q_tilde
-        f32x4 qt[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) qt[c] = ld4(qt_l + pos * kDim + 4 * lane8 + 32 * c);
-        f32x4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(h[r][c][e], qt[c][e], acc);
-            o[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = sum8(o[r]);
-
-        if (lane8 == 0) {
-            st4(p.out + ((int64_t)ts + t) * p.o_ts + hv * p.o_hs + 4 * grp, o);
-            if constexpr (!SNAP) st4(recb + pos * kDim + 4 * grp, d);
-        }
-        if constexpr (SNAP) {
-            StateT* sn = static_cast<StateT*>(p.snap) +
-                         (((int64_t)b * p.hv + hv) * T + t) * kHeadElems;
-            TileIO<StateT>::store(sn, grp, lane8, h);
+                    for (int e = 0; e < 4; ++e) h[r][c][e] = __builtin_fmaf(d, kh[c][e], h[r][c][e] * g);
+            }
+            StateT* sn = static_cast<StateT*>(p.snap) + (((int64_t)b * p.hv + hv) * T + t) * kHeadElems;
+            TileIO<StateT, R>::store(sn, row0, grp, lane8, h);
         }
     }
 }
 
-template <typename StateT, bool SNAP>
+template <typename StateT, bool SNAP, int R>
 hipError_t launch(const VerifyParams& p, hipStream_t s)
 {
     VerifyParams args = p;
     void* kargs[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP>),
-                           dim3((unsigned)(p.num_rows * p.hv)), dim3(kThreads), kargs,
-                           verify_lds_bytes(p.T), s);
+    const unsigned grid = (unsigned)(p.num_rows * p.hv) * (unsigned)(kDim / (32 * R));
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R>),
+                           dim3(grid), dim3(kThreads), kargs, verify_lds_bytes(p.T), s);
+}
+
+template <bool SNAP, int R>
+hipError_t launch_dtype(const VerifyParams& p, bool bf16_state, hipStream_t s)
+{
+    return bf16_state ? launch<uint16_t, SNAP, R>(p, s) : launch<float, SNAP, R>(p, s);
 }
 
 }  // namespace
 
+hipError_t launch_verify_rows(const VerifyParams& p, bool bf16_state, bool snap, int R,
+                              hipStream_t s)
+{
+    switch ((snap ? 8 : 0) + R) {
+    case 4: return launch_dtype<false, 4>(p, bf16_state, s);
+    case 2: return launch_dtype<false, 2>(p, bf16_state, s);
+    case 1: return launch_dtype<false, 1>(p, bf16_state, s);
+    case 12: return launch_dtype<true, 4>(p, bf16_state, s);
+    case 10: return launch_dtype<true, 2>(p, bf16_state, s);
+    case 9: return launch_dtype<true, 1>(p, bf16_state, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return bf16_state ? launch<uint16_t, false>(p, s) : launch<float, false>(p, s);
+    return launch_verify_rows(p, bf16_state, false, kVerifyRowsPerThread, s);
 }
 
 hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return bf16_state ? launch<uint16_t, true>(p, s) : launch<float, true>(p, s);
+    return launch_verify_rows(p, bf16_state, true, kVerifyRowsPerThread, s);
 }
 
 }  // namespace gdn

@@ -201,10 +201,10 @@ def make_workload(spec: WorkloadSpec, device="cpu", state_dtype=torch.float32,
             r[i * 4: i * 4 + 4] = rv
         rng.shuffle(r)
         p0 = (m * blk + r).astype(np.int32)
-        cols = int((p0.max() + spec.ring_steps - 1) // blk) + 1
+        c0 = (p0 - 1) // blk                          # the checkpoint's block column
+        cols = int(c0.max()) + 2                      # room for the next block of every row
         slots = rng.permutation(spec.num_slots)[: 2 * B].astype(np.int32).reshape(B, 2)
         table = np.full((B, cols), -1, np.int32)
-        c0 = (p0 - 1) // blk
         table[np.arange(B), c0] = slots[:, 0]
         table[np.arange(B), c0 + 1] = slots[:, 1]
         wl.p0 = p0

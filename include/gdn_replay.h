@@ -56,7 +56,7 @@ extern "C" {
 #define GDN_ABI_VERSION 1
 #define GDN_MAX_LAYERS 64      /* layers per pool set */
 #define GDN_HEAD_DIM 128       /* K = V = 128 */
-#define GDN_MAX_REC_TOKENS 32  /* record capacity T per row */
+#define GDN_MAX_REC_TOKENS 16  /* record capacity T per row */
 
 typedef enum {
     GDN_OK = 0,

@@ -97,7 +97,7 @@ def test_verify_zero_rows_is_ok_without_launch(lib):
     (lambda p, io: setattr(p, "num_layers", 0), E_SHAPE),
     (lambda p, io: setattr(p, "num_layers", 65), E_SHAPE),
     (lambda p, io: setattr(p, "rec_tokens", 0), E_SHAPE),
-    (lambda p, io: setattr(p, "rec_tokens", 33), E_SHAPE),
+    (lambda p, io: setattr(p, "rec_tokens", 17), E_SHAPE),
     (lambda p, io: setattr(p, "num_state_slots", 0), E_SHAPE),
     (lambda p, io: setattr(p, "state_dtype", 2), E_DTYPE),
     (lambda p, io: p.state.__setitem__(0, 0), E_NULL),

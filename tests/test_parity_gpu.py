@@ -2,9 +2,14 @@
 
 Bars (vLLM RecoverSSM PR, Test Plan and Test Result; the tolerance is the
 1e-5 relative error the method's fp32 states and outputs must meet):
-  * fp32 states, outputs and records: normwise relative error per block
-    (max|x - y| / max|y| over one state head, one output vector, one record
-    vector) <= 1e-5 against the oracle's native per-token rule;
+  * fp32 states, outputs and records: normwise relative error of each layer's
+    result (max|x - y| / max|y| over the layer's outputs, over each record
+    field, over its committed state heads) <= 1e-5 against the oracle's native
+    per-token rule. A single output vector can cancel to a small value whose
+    own relative error is set by fp32 rounding alone (the fp32 oracle is off
+    from fp64 by 1e-5 on such vectors), so the per-vector accuracy is checked
+    separately: the GPU is no less accurate than the fp32 oracle, both against
+    the fp64 instantiation of the oracle;
   * the commit against the oracle's replay of the GPU's own records: bit-exact
     (the replay is elementwise, so there is no reduction order to differ in);
   * slots, plans and write sets: bit-exact;
@@ -38,8 +43,10 @@ def assert_bitwise(x, y, what=""):
     assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} differ"
 
 
-def assert_close(x, y, ndim, what=""):
-    err = OP.relerr_blocks(x, y, ndim)
+def assert_close(x, y, what=""):
+    """Normwise relative error of the whole compared tensor <= TOL."""
+    x = np.asarray(x)
+    err = OP.relerr_blocks(x, y, x.ndim)
     assert err <= TOL, f"{what}: normwise relative error {err:.3e} > {TOL}"
 
 
@@ -65,13 +72,13 @@ def check_layer(h, layer, rows, n, pre_state, *, T=None, bnd=None, dst=None, che
     valid = np.arange(Tw)[None, :] < w[:, None]
     if check_out:
         o = h.outputs(layer, rows, T)
-        assert_close(np.where(valid[..., None], o, 0), np.where(valid[..., None], res.o, 0), 1,
+        assert_close(np.where(valid[..., None], o, 0), np.where(valid[..., None], res.o, 0),
                      f"layer {layer} outputs")
     d, kh, gg = h.records(layer, rows)
     d, kh, gg = d[:, :Tw], kh[:, :Tw], gg[:, :Tw]
-    assert_close(np.where(valid[..., None], d, 0), res.rec_delta, 1, f"layer {layer} corrections")
-    assert_close(np.where(valid[..., None], kh, 0), res.rec_khat, 1, f"layer {layer} keys")
-    assert_close(np.where(valid, gg, 0), res.rec_g, 1, f"layer {layer} gates")
+    assert_close(np.where(valid[..., None], d, 0), res.rec_delta, f"layer {layer} corrections")
+    assert_close(np.where(valid[..., None], kh, 0), res.rec_khat, f"layer {layer} keys")
+    assert_close(np.where(valid, gg, 0), res.rec_g, f"layer {layer} gates")
     n_h = np.repeat(n, s.hv)
     # final state: within tolerance of the native rule, bit-exact vs replay of the GPU records
     dst = wl.state_slot[rows] if dst is None else np.asarray(dst)
@@ -85,7 +92,7 @@ def check_layer(h, layer, rows, n, pre_state, *, T=None, bnd=None, dst=None, che
         rep = oracle.replay_heads(g["S0"][live_h], n_h[live_h], d_f[live_h], k_f[live_h],
                                   g_f[live_h])
         if h.wl.state_dtype == torch.float32:
-            assert_close(got, res.kept[live_h, 0], 2, f"layer {layer} final states")
+            assert_close(got, res.kept[live_h, 0], f"layer {layer} final states")
             assert_bitwise(got, rep, f"layer {layer} final state vs replay of GPU records")
         else:
             check_bf16(h, layer, dst[live], rep, res.kept[live_h, 0], "final")
@@ -98,7 +105,7 @@ def check_layer(h, layer, rows, n, pre_state, *, T=None, bnd=None, dst=None, che
                 repb = oracle.replay_heads(g["S0"][has_h], np.repeat(bl[has], s.hv), d_f[has_h],
                                            k_f[has_h], g_f[has_h])
                 if h.wl.state_dtype == torch.float32:
-                    assert_close(gotb, res.kept[has_h, 1], 2, f"layer {layer} boundary states")
+                    assert_close(gotb, res.kept[has_h, 1], f"layer {layer} boundary states")
                     assert_bitwise(gotb, repb, f"layer {layer} boundary vs replay of GPU records")
                 else:
                     check_bf16(h, layer, bs[has], repb, res.kept[has_h, 1], "boundary")
@@ -317,19 +324,23 @@ def test_bf16_verify_is_exact(gdn):
 
 
 def test_onehot_bitwise(gdn):
-    """One-hot q and k, gates exp(0) = 1 or exp(-inf) = 0: single-term
-    reductions, so outputs, records and committed states equal the oracle
-    exactly. A transposed state layout or a wrong key-head map fails here."""
+    """One-hot q and k, gates exp(0) = 1 or exp(-inf) = 0. Within each row's
+    window the keys sit on distinct columns and the queries on other columns,
+    so every reduction and every cross-token term has one non-zero term (or
+    none) and GPU and oracle agree exactly. A transposed state layout or a
+    wrong key-head map fails here."""
     spec = W.SINGLE_LAYER
     wl = W.make_workload(spec, device="cuda", seed=21)
     rng = np.random.default_rng(21)
-    T, HK = wl.tokens, spec.hk
-    qi = rng.integers(0, 128, size=(T, HK))
-    ki = rng.integers(0, 128, size=(T, HK))
+    T, HK, D = wl.tokens, spec.hk, spec.window
     q = np.zeros((T, HK, 128), np.float32)
     k = np.zeros((T, HK, 128), np.float32)
-    q[np.arange(T)[:, None], np.arange(HK)[None], qi] = 1.0
-    k[np.arange(T)[:, None], np.arange(HK)[None], ki] = 1.0
+    for b in range(spec.rows):
+        for hk in range(HK):
+            cols = rng.permutation(128)[: 2 * D]
+            for t in range(D):
+                k[wl.tok_start[b] + t, hk, cols[t]] = 1.0
+                q[wl.tok_start[b] + t, hk, cols[D + t]] = 1.0
     wl.qkv[0, :, : HK * 128] = torch.as_tensor(q.reshape(T, -1)).to(torch.bfloat16).cuda()
     wl.qkv[0, :, HK * 128: 2 * HK * 128] = torch.as_tensor(k.reshape(T, -1)).to(torch.bfloat16).cuda()
     a = np.where(rng.random((T, spec.hv)) < 0.3, -np.inf, 0.0).astype(np.float32)
@@ -376,7 +387,7 @@ def test_output_scale(gdn):
     torch.cuda.synchronize()
     rows = np.arange(spec.rows)
     g, res = OP.run_layer(wl, 0, rows, scale=128 ** -0.5)
-    assert_close(h.outputs(0, rows), res.o, 1, "scaled outputs")
+    assert_close(h.outputs(0, rows), res.o, "scaled outputs")
 
 
 def test_ragged_windows_strided_output_noncontiguous_rows(gdn):
@@ -468,14 +479,42 @@ def test_align_plan_matches_oracle(gdn):
             assert np.array_equal(got.cpu().numpy(), exp)
         assert int(err.item()) == int(np.bitwise_or.reduce(want[4]))
     # error rows, one cause each
-    p0 = np.array([0, 10, 10, 3], np.int32)
-    n = np.array([1, 7, 2, 9], np.int32)
     table = np.tile(np.array([1, 2, -1], np.int32), (4, 1))
     outs = [torch.empty(4, dtype=torch.int32, device="cuda") for _ in range(4)]
-    for i, (pp, nn, cause) in enumerate(((0, 1, 64), (10, 7, 4), (11, 2, 16), (3, 9, 8))):
+    for pp, nn, max_n, cause in ((0, 1, 6, 64), (10, 7, 6, 4), (11, 2, 6, 16), (3, 9, 16, 8)):
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
-        G.gdn_align_plan(dev_i32([pp]), dev_i32([nn]), dev_i32(table[:1]), 4, 6 if cause != 4 else 6,
+        G.gdn_align_plan(dev_i32([pp]), dev_i32([nn]), dev_i32(table[:1]), 4, max_n,
                          *[o[:1] for o in outs], err_flags=err)
-        want = oracle.align_plan([pp], [nn], table[:1], 4, 6)
+        want = oracle.align_plan([pp], [nn], table[:1], 4, max_n)
         assert int(err.item()) == cause == int(want[4][0]), (pp, nn)
         assert [int(o[0].item()) for o in outs] == [-1, -1, 0, -1]
+
+
+def test_accuracy_against_fp64(gdn):
+    """Per output vector and per state head, the GPU's error against the fp64
+    instantiation of the oracle is no larger than the fp32 oracle's own
+    (within a factor 2), and both are far inside 1e-5 normwise."""
+    spec = W.shrink(W.ALL_LAYER, layers=4)
+    wl = W.make_workload(spec, device="cuda", seed=71)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    rows = np.arange(spec.rows)
+    for layer in range(spec.layers):
+        g = OP.gather(wl, layer, rows, state=pre[layer])
+        keep = np.repeat(wl.n_accept, spec.hv)[:, None]
+        args = (g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"])
+        r32 = oracle.native_heads(*args, keep=keep)
+        r64 = oracle.native_heads(*args, keep=keep, dtype=np.float64)
+        o_gpu = h.outputs(layer, rows).astype(np.float64)
+        S_gpu = h.heads(layer, wl.state_slot).astype(np.float64)
+        for name, gpu, o32, o64, ax in (
+                ("outputs", o_gpu, r32.o, r64.o, (-1,)),
+                ("states", S_gpu, r32.kept[:, 0], r64.kept[:, 0], (-1, -2))):
+            e_gpu = np.abs(gpu - o64).max(axis=ax) / np.abs(o64).max(axis=ax)
+            e_32 = np.abs(o32.astype(np.float64) - o64).max(axis=ax) / np.abs(o64).max(axis=ax)
+            assert e_gpu.max() <= 2 * e_32.max() + 1e-7, (layer, name, e_gpu.max(), e_32.max())
+            assert np.percentile(e_gpu, 99) <= 2 * np.percentile(e_32, 99) + 1e-7, (layer, name)
+            assert OP.relerr_blocks(gpu, o64, gpu.ndim) <= 1e-6, (layer, name)
