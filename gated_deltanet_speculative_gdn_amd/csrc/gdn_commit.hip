@@ -281,7 +281,8 @@ hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool alig
 
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s)
 {
-    return launch_commit_shape(p, bf16_state, align, kCommitSplit, kCommitNontemporal, s);
+    return launch_commit_shape(p, bf16_state, align, bf16_state ? kCommitSplitBf16 : kCommitSplitF32,
+                               kCommitNontemporal, s);
 }
 
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s)

@@ -78,6 +78,16 @@ __device__ __forceinline__ f32x4 ld4_nt(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
+// Uniform read of a kernel input the kernel never writes (row metadata):
+// through the constant address space with a wave-uniform index it becomes a
+// scalar load, which waits on its own counter rather than on the vector loads
+// in flight.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* base, int idx) {
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    const int i = __builtin_amdgcn_readfirstlane(idx);
+    return ((cint32*)base)[i];
+}
+
 // The dispatcher hands workgroup w to XCD w % 8 (eight XCDs, each with its
 // own L2). Remapping w so that the workgroups one XCD receives take one
 // contiguous range of logical ids lets each XCD stream a contiguous stretch of

@@ -70,18 +70,22 @@ struct PlanParams {
     int32_t num_rows, cols, block, max_n;
 };
 
-// Rows of a head each verify thread holds (4, 2 or 1): a head is split over
-// 4/R workgroups of 256 threads.
+// Verify launch shape: rows of a head each thread holds (4, 2 or 1) and
+// threads per workgroup (256 or 512); a workgroup covers threads/8 * R rows.
 constexpr int kVerifyRowsPerThread = 2;
-// Commit: workgroups per head (1, 2, 4 or 8); whether state loads and stores
-// are nontemporal; whether workgroup ids are remapped XCD-contiguous.
-constexpr int kCommitSplit = 1;
+constexpr int kVerifyThreads = 256;
+// Commit: workgroups per head (1, 2, 4 or 8) for fp32 and bf16 pools (16 KiB
+// per workgroup streams best for fp32, a whole 32 KiB head for bf16); whether
+// state loads and stores are nontemporal; whether workgroup ids are remapped
+// XCD-contiguous.
+constexpr int kCommitSplitF32 = 4;
+constexpr int kCommitSplitBf16 = 1;
 constexpr bool kCommitNontemporal = true;
 constexpr bool kCommitXcdRemap = true;
 
 // Launchers: return the hipError_t of the launch.
-hipError_t launch_verify_rows(const VerifyParams& p, bool bf16_state, bool snap, int R,
-                              hipStream_t s);
+hipError_t launch_verify_shape(const VerifyParams& p, bool bf16_state, bool snap, int R,
+                               int threads, hipStream_t s);
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s);
@@ -93,7 +97,7 @@ hipError_t launch_align_plan(const PlanParams& p, hipStream_t s);
 // Dynamic LDS of the verify kernel for record capacity T (bytes).
 inline size_t verify_lds_bytes(int T)
 {
-    return sizeof(float) * (4 * (size_t)T * 128 + 3 * (size_t)T + 2 * (size_t)T * T);
+    return sizeof(float) * (5 * (size_t)T * 128 + 3 * (size_t)T + 2 * (size_t)T * T);
 }
 inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + (size_t)T); }
 

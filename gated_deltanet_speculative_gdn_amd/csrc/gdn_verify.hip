@@ -118,24 +118,28 @@ __device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x,
 //   vd   [T][128]  ring positions: recorded corrections; window positions: values
 //   qt   [T][128]  window positions: normalised, scaled queries
 //   dw   [T][128]  window positions: the corrections computed here
+//   ob   [T][128]  window positions: the outputs (written out coalesced at the end)
 //   g [T], be [T], g0 [T] = G(0, p+1)
 //   ca [T][T] = G(j+1, p+1) (k_j . k_p), j < p;  cb [T][T] = G(j+1, p+1) (k_j . q_p), j <= p
 struct Lds {
-    float *khat, *vd, *qt, *dw, *g, *be, *g0, *ca, *cb;
+    float *khat, *vd, *qt, *dw, *ob, *g, *be, *g0, *ca, *cb;
     __device__ Lds(float* base, int T)
         : khat(base), vd(base + T * kDim), qt(base + 2 * T * kDim), dw(base + 3 * T * kDim),
-          g(base + 4 * T * kDim), be(g + T), g0(be + T), ca(g0 + T), cb(ca + T * T) {}
+          ob(base + 4 * T * kDim), g(base + 5 * T * kDim), be(g + T), g0(be + T), ca(g0 + T),
+          cb(ca + T * T) {}
 };
 
-// R = rows of the head per thread; a workgroup covers 32*R rows, so a head is
-// split over 4/R workgroups. Each stages the whole window (the norms and dot
-// products need all 128 columns); the head-level record fields (key, gate) are
-// written by the first chunk.
-template <typename StateT, bool SNAP, int R>
-__global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
+// NT threads per workgroup, R rows of the head per thread: a workgroup covers
+// NT/8 * R rows, so a head is split over kChunks workgroups. Each stages the
+// whole window (the norms and dot products need all 128 columns); the
+// head-level record fields (key, gate) are written by the first chunk.
+template <typename StateT, bool SNAP, int R, int NT>
+__global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 {
     static_assert(R == 1 || R == 2 || R == 4, "rows per thread");
-    constexpr int kChunks = kDim / (32 * R);
+    constexpr int kRowsPerWg = NT / 8 * R;
+    static_assert(kDim % kRowsPerWg == 0, "workgroup rows divide the head");
+    constexpr int kChunks = kDim / kRowsPerWg;
     extern __shared__ float lds_raw[];
     const int T = p.T;
     const Lds L(lds_raw, T);
@@ -145,18 +149,18 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
     const int64_t bh = item / kChunks;
     const int b = (int)(bh / p.hv);
     const int hv = (int)(bh - (int64_t)b * p.hv);
-    const int row0 = chunk * 32 * R;
+    const int row0 = chunk * kRowsPerWg;
     const bool lead = chunk == 0;
 
     // ---- row decode: a null slot or an empty window is padding ----
-    const int slot = p.state_slot[b];
-    const int w = p.win_len[b];
+    const int slot = ld_uniform(p.state_slot, b);
+    const int w = ld_uniform(p.win_len, b);
     if (slot < 0 || w == 0) return;
-    const int ts = p.tok_start[b];
+    const int ts = ld_uniform(p.tok_start, b);
     int j0 = 0, rs = 0;
     if constexpr (!SNAP) {
-        j0 = p.rec_base ? p.rec_base[b] : 0;
-        rs = p.rec_slot[b];
+        j0 = p.rec_base ? ld_uniform(p.rec_base, b) : 0;
+        rs = ld_uniform(p.rec_slot, b);
     }
     int err = 0;
     if (slot >= p.num_slots) err |= kRowSlot;
@@ -206,7 +210,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         // pending ring records (positions 0 .. j0-1): at most 2 pieces per thread (T <= 16)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int i = tid + q * kThreads;
+            const int i = tid + q * NT;
             if (i < j0 * (kDim / 4)) {
                 ring_d[q] = ld4(recb + 4 * i);
                 ring_k[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
@@ -222,7 +226,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
     if constexpr (!SNAP) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int i = tid + q * kThreads;
+            const int i = tid + q * NT;
             if (i < j0 * (kDim / 4)) {
                 st4(L.vd + 4 * i, ring_d[q]);
                 st4(L.khat + 4 * i, ring_k[q]);
@@ -230,7 +234,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         }
         if (tid < j0) L.g[tid] = ring_g;
     }
-    for (int jb = jb0; jb < 3 * w; jb += kThreads / 16) {
+    for (int jb = jb0; jb < 3 * w; jb += NT / 16) {
         const int t = jb / 3;
         const int kind = jb - 3 * t;
         const u32x4 raw = jb == jb0 ? raw0 : *reinterpret_cast<const u32x4*>(job_src(jb) + 8 * lane16);
@@ -264,7 +268,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
             }
         }
     }
-    for (int t = tid; t < w; t += kThreads) {
+    for (int t = tid; t < w; t += NT) {
         float av = a_in, bv = b_in;
         if (t != tid) {          // windows longer than the workgroup (not reachable at T <= 16)
             const int64_t tok = (int64_t)ts + t;
@@ -282,7 +286,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
     // Window position p has 2p + 1 dot-product jobs: (k_j . k_p) for j < p, then
     // (k_j . q_p) for j <= p; jobs of p start at p^2 - j0^2.
     const int njobs = P * P - j0 * j0;
-    for (int jb = tid >> 4; jb < njobs; jb += kThreads / 16) {
+    for (int jb = tid >> 4; jb < njobs; jb += NT / 16) {
         int pp = j0;
         while ((pp + 1) * (pp + 1) - j0 * j0 <= jb) ++pp;
         const int rem = jb - (pp * pp - j0 * j0);
@@ -301,7 +305,7 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
         for (int m = j + 1; m <= pp; ++m) gam = gam * L.g[m];
         if (lane16 == 0) (is_q ? L.cb : L.ca)[j * T + pp] = gam * dot;
     }
-    for (int t = tid; t < w; t += kThreads) {
+    for (int t = tid; t < w; t += NT) {
         float gam = 1.f;
         for (int m = 0; m <= j0 + t; ++m) gam = gam * L.g[m];
         L.g0[j0 + t] = gam;
@@ -345,14 +349,20 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cpp, d[r], o[r]);
 
-        // lane r of the row group stores row r
-        float* orow = p.out + ((int64_t)ts + (pp - j0)) * p.o_ts + hv * p.o_hs + rbase;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (lane8 == r) {
-                orow[r] = o[r];
-                if constexpr (!SNAP) recb[pp * kDim + rbase + r] = d[r];
-            }
+        for (int r = 0; r < R; ++r) L.ob[pp * kDim + rbase + r] = o[r];   // same value in all 8 lanes
+    }
+    __syncthreads();
+
+    // ---- outputs and corrections of the owned rows, written out coalesced ----
+    {
+        constexpr int kRow4 = kRowsPerWg / 4;
+        for (int i = tid; i < w * kRow4; i += NT) {
+            const int t = i / kRow4;
+            const int c = 4 * (i - t * kRow4);
+            st4(p.out + ((int64_t)ts + t) * p.o_ts + (int64_t)hv * p.o_hs + row0 + c,
+                ld4(L.ob + (j0 + t) * kDim + row0 + c));
+            if constexpr (!SNAP) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kDim + row0 + c));
         }
     }
 
@@ -377,46 +387,53 @@ __global__ void __launch_bounds__(kThreads) verify_kernel(VerifyParams p)
     }
 }
 
-template <typename StateT, bool SNAP, int R>
+template <typename StateT, bool SNAP, int R, int NT>
 hipError_t launch(const VerifyParams& p, hipStream_t s)
 {
     VerifyParams args = p;
     void* kargs[] = {&args};
-    const unsigned grid = (unsigned)(p.num_rows * p.hv) * (unsigned)(kDim / (32 * R));
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R>),
-                           dim3(grid), dim3(kThreads), kargs, verify_lds_bytes(p.T), s);
+    const unsigned chunks = kDim / (NT / 8 * R);
+    const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT>),
+                           dim3(grid), dim3(NT), kargs, verify_lds_bytes(p.T), s);
 }
 
-template <bool SNAP, int R>
+template <bool SNAP, int R, int NT>
 hipError_t launch_dtype(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return bf16_state ? launch<uint16_t, SNAP, R>(p, s) : launch<float, SNAP, R>(p, s);
+    return bf16_state ? launch<uint16_t, SNAP, R, NT>(p, s) : launch<float, SNAP, R, NT>(p, s);
 }
 
-}  // namespace
-
-hipError_t launch_verify_rows(const VerifyParams& p, bool bf16_state, bool snap, int R,
-                              hipStream_t s)
+template <bool SNAP>
+hipError_t launch_shape(const VerifyParams& p, bool bf16_state, int R, int threads, hipStream_t s)
 {
-    switch ((snap ? 8 : 0) + R) {
-    case 4: return launch_dtype<false, 4>(p, bf16_state, s);
-    case 2: return launch_dtype<false, 2>(p, bf16_state, s);
-    case 1: return launch_dtype<false, 1>(p, bf16_state, s);
-    case 12: return launch_dtype<true, 4>(p, bf16_state, s);
-    case 10: return launch_dtype<true, 2>(p, bf16_state, s);
-    case 9: return launch_dtype<true, 1>(p, bf16_state, s);
+    switch (R * 1000 + threads) {
+    case 4256: return launch_dtype<SNAP, 4, 256>(p, bf16_state, s);
+    case 2256: return launch_dtype<SNAP, 2, 256>(p, bf16_state, s);
+    case 1256: return launch_dtype<SNAP, 1, 256>(p, bf16_state, s);
+    case 2512: return launch_dtype<SNAP, 2, 512>(p, bf16_state, s);
+    case 1512: return launch_dtype<SNAP, 1, 512>(p, bf16_state, s);
     default: return hipErrorInvalidValue;
     }
 }
 
+}  // namespace
+
+hipError_t launch_verify_shape(const VerifyParams& p, bool bf16_state, bool snap, int R,
+                               int threads, hipStream_t s)
+{
+    return snap ? launch_shape<true>(p, bf16_state, R, threads, s)
+                : launch_shape<false>(p, bf16_state, R, threads, s);
+}
+
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return launch_verify_rows(p, bf16_state, false, kVerifyRowsPerThread, s);
+    return launch_verify_shape(p, bf16_state, false, kVerifyRowsPerThread, kVerifyThreads, s);
 }
 
 hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return launch_verify_rows(p, bf16_state, true, kVerifyRowsPerThread, s);
+    return launch_verify_shape(p, bf16_state, true, kVerifyRowsPerThread, kVerifyThreads, s);
 }
 
 }  // namespace gdn
