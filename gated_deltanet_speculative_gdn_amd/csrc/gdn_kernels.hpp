@@ -70,6 +70,8 @@ struct PlanParams {
     int32_t num_rows, cols, block, max_n;
 };
 
+constexpr int kMaxRecTokens = GDN_MAX_REC_TOKENS;
+
 // Verify launch shape: rows of a head each thread holds (4, 2 or 1) and
 // threads per workgroup (256 or 512); a workgroup covers threads/8 * R rows.
 constexpr int kVerifyRowsPerThread = 2;

@@ -113,27 +113,28 @@ __device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x,
     for (int r = 0; r < R; ++r) out[r] = sum8(out[r]);
 }
 
-// LDS layout of one workgroup (floats), T = record capacity:
-//   khat [T][128]  normalised keys of every position (ring records and window)
-//   vd   [T][128]  ring positions: recorded corrections; window positions: values
-//   qt   [T][128]  window positions: normalised, scaled queries
-//   dw   [T][128]  window positions: the corrections computed here
-//   ob   [T][128]  window positions: the outputs (written out coalesced at the end)
-//   g [T], be [T], g0 [T] = G(0, p+1)
-//   ca [T][T] = G(j+1, p+1) (k_j . k_p), j < p;  cb [T][T] = G(j+1, p+1) (k_j . q_p), j <= p
-struct Lds {
+// LDS layout of one workgroup (floats), TT = compile-time window capacity
+// (>= the record capacity T), so every LDS offset is an immediate:
+//   khat [TT][128]  normalised keys of every position (ring records and window)
+//   vd   [TT][128]  ring positions: recorded corrections; window positions: values
+//   qt   [TT][128]  window positions: normalised, scaled queries
+//   dw   [TT][128]  window positions: the corrections computed here
+//   ob   [TT][128]  window positions: the outputs (written out coalesced at the end)
+//   g [TT], be [TT], g0 [TT] = G(0, p+1)
+//   ca [TT][TT] = G(j+1, p+1) (k_j . k_p), j < p;  cb [TT][TT] = G(j+1, p+1) (k_j . q_p), j <= p
+template <int TT> struct Lds {
     float *khat, *vd, *qt, *dw, *ob, *g, *be, *g0, *ca, *cb;
-    __device__ Lds(float* base, int T)
-        : khat(base), vd(base + T * kDim), qt(base + 2 * T * kDim), dw(base + 3 * T * kDim),
-          ob(base + 4 * T * kDim), g(base + 5 * T * kDim), be(g + T), g0(be + T), ca(g0 + T),
-          cb(ca + T * T) {}
+    __device__ explicit Lds(float* base)
+        : khat(base), vd(base + TT * kDim), qt(base + 2 * TT * kDim), dw(base + 3 * TT * kDim),
+          ob(base + 4 * TT * kDim), g(base + 5 * TT * kDim), be(g + TT), g0(be + TT), ca(g0 + TT),
+          cb(ca + TT * TT) {}
 };
 
 // NT threads per workgroup, R rows of the head per thread: a workgroup covers
 // NT/8 * R rows, so a head is split over kChunks workgroups. Each stages the
 // whole window (the norms and dot products need all 128 columns); the
 // head-level record fields (key, gate) are written by the first chunk.
-template <typename StateT, bool SNAP, int R, int NT>
+template <typename StateT, bool SNAP, int R, int NT, int TT>
 __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 {
     static_assert(R == 1 || R == 2 || R == 4, "rows per thread");
@@ -141,8 +142,8 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     static_assert(kDim % kRowsPerWg == 0, "workgroup rows divide the head");
     constexpr int kChunks = kDim / kRowsPerWg;
     extern __shared__ float lds_raw[];
-    const int T = p.T;
-    const Lds L(lds_raw, T);
+    const int T = p.T;   // record capacity (record addressing); T <= TT
+    const Lds<TT> L(lds_raw);
 
     const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int chunk = (int)(item % kChunks);
@@ -303,7 +304,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         dot = sum16(dot);
         float gam = 1.f;
         for (int m = j + 1; m <= pp; ++m) gam = gam * L.g[m];
-        if (lane16 == 0) (is_q ? L.cb : L.ca)[j * T + pp] = gam * dot;
+        if (lane16 == 0) (is_q ? L.cb : L.ca)[j * TT + pp] = gam * dot;
     }
     for (int t = tid; t < w; t += NT) {
         float gam = 1.f;
@@ -312,43 +313,47 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     }
     __syncthreads();
 
-    // ---- the window, position by position ----
+    // ---- the window, position by position (unrolled over the capacity TT;
+    // the corrections of the owned rows stay in registers) ----
     const int rbase = row0 + R * grp;
-    for (int pp = j0; pp < P; ++pp) {
+    float dreg[TT][R];
+#pragma unroll
+    for (int pp = 0; pp < TT; ++pp) {
+        if (pp < j0) {                 // ring position: its recorded correction
+#pragma unroll
+            for (int r = 0; r < R; ++r) dreg[pp][r] = L.vd[pp * kDim + rbase + r];
+            continue;
+        }
+        if (pp >= P) break;
         const float g0 = L.g0[pp];
         float pk[R];
         tile_dot<R>(h, L.khat + pp * kDim, lane8, pk);
         float u[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) u[r] = g0 * pk[r];
-        for (int j = 0; j < pp; ++j) {
-            const float cf = L.ca[j * T + pp];
-            const float* dj = (j < j0 ? L.vd : L.dw) + j * kDim + rbase;
 #pragma unroll
-            for (int r = 0; r < R; ++r) u[r] = __builtin_fmaf(cf, dj[r], u[r]);
+        for (int j = 0; j < pp; ++j) {
+            const float cf = L.ca[j * TT + pp];
+#pragma unroll
+            for (int r = 0; r < R; ++r) u[r] = __builtin_fmaf(cf, dreg[j][r], u[r]);
         }
         const float be = L.be[pp];
-        float d[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) d[r] = be * (L.vd[pp * kDim + rbase + r] - u[r]);
+        for (int r = 0; r < R; ++r) dreg[pp][r] = be * (L.vd[pp * kDim + rbase + r] - u[r]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) L.dw[pp * kDim + rbase + r] = d[r];   // same value in all 8 lanes
+        for (int r = 0; r < R; ++r) L.dw[pp * kDim + rbase + r] = dreg[pp][r];  // same value in all 8 lanes
 
         float pq[R];
         tile_dot<R>(h, L.qt + pp * kDim, lane8, pq);
         float o[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = g0 * pq[r];
-        for (int j = 0; j < pp; ++j) {
-            const float cf = L.cb[j * T + pp];
-            const float* dj = (j < j0 ? L.vd : L.dw) + j * kDim + rbase;
 #pragma unroll
-            for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cf, dj[r], o[r]);
+        for (int j = 0; j <= pp; ++j) {
+            const float cf = L.cb[j * TT + pp];
+#pragma unroll
+            for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cf, dreg[j][r], o[r]);
         }
-        const float cpp = L.cb[pp * T + pp];
-#pragma unroll
-        for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cpp, d[r], o[r]);
-
 #pragma unroll
         for (int r = 0; r < R; ++r) L.ob[pp * kDim + rbase + r] = o[r];   // same value in all 8 lanes
     }
@@ -368,14 +373,16 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 
     // ---- native baseline: materialise and write S_1..S_w ----
     if constexpr (SNAP) {
-        for (int t = 0; t < w; ++t) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if (t >= w) break;
             const float g = L.g[t];
             f32x4 kh[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float d = L.dw[t * kDim + rbase + r];
+                const float d = dreg[t][r];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -387,15 +394,24 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     }
 }
 
-template <typename StateT, bool SNAP, int R, int NT>
-hipError_t launch(const VerifyParams& p, hipStream_t s)
+template <typename StateT, bool SNAP, int R, int NT, int TT>
+hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
 {
     VerifyParams args = p;
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT>),
-                           dim3(grid), dim3(NT), kargs, verify_lds_bytes(p.T), s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT>),
+                           dim3(grid), dim3(NT), kargs, verify_lds_bytes(TT), s);
+}
+
+// The smallest compile-time window capacity that holds the record capacity.
+template <typename StateT, bool SNAP, int R, int NT>
+hipError_t launch(const VerifyParams& p, hipStream_t s)
+{
+    if (p.T <= 4) return launch_tt<StateT, SNAP, R, NT, 4>(p, s);
+    if (p.T <= 8) return launch_tt<StateT, SNAP, R, NT, 8>(p, s);
+    return launch_tt<StateT, SNAP, R, NT, kMaxRecTokens>(p, s);
 }
 
 template <bool SNAP, int R, int NT>
