@@ -135,9 +135,9 @@ def timed_loop(steps, graph_fn, eager_fn, graph_launches):
         e2.record()
     sync()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    # per-launch times: medians over the timed steps (robust to clock transients)
-    g_ms = float(np.median([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    c_ms = float(np.median([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    # per-launch times: averages over the timed steps
+    g_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    c_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
     return wall, g_ms / graph_launches, c_ms, g_ms
 
 
@@ -148,28 +148,38 @@ def capture(fn):
     return g
 
 
-def cpu_baseline(wl, acc):
-    """The oracle (plain C, OpenMP over heads) on one full step of the same
-    workload: every layer's real rows, windows and accepted counts."""
+def cpu_baseline(wl, acc, target_s=15.0):
+    """The oracle (plain C, OpenMP over heads) on the same workload: every
+    layer's real rows, windows and accepted counts, the whole step repeated
+    until about `target_s` seconds of oracle time (the count is fixed from the
+    first layer's time)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     import oracle_pool as OP
     s = wl.spec
     real = np.nonzero((wl.state_slot >= 0) & (wl.win_len > 0))[0]
     nthreads = oracle.default_threads()
-    spent = 0.0
-    for layer in range(s.layers):
-        g = OP.gather(wl, layer, real)
-        keep = np.repeat(wl.n_accept[real], s.hv)[:, None]
+    keep = np.repeat(wl.n_accept[real], s.hv)[:, None]
+
+    def run(g):
         t0 = time.perf_counter()
         oracle.native_heads(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
                             keep=keep, nthreads=nthreads)
-        spent += time.perf_counter() - t0
-    updates = acc["verify_updates"] + acc["commit_updates"]
+        return time.perf_counter() - t0
+
+    g = OP.gather(wl, 0, real)
+    first = run(g)
+    reps = max(1, int(np.ceil(target_s / (first * s.layers))))
+    spent = first + sum(run(g) for _ in range(reps - 1))
+    for layer in range(1, s.layers):
+        g = OP.gather(wl, layer, real)
+        spent += sum(run(g) for _ in range(reps))
+    updates = reps * (acc["verify_updates"] + acc["commit_updates"])
     return {"value": updates / spent, "unit": "state-updates/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(spent, 3),
-            "sample": f"one full step of {s.name}: {s.layers} layers x {len(real)} rows x "
-                      f"{s.hv} heads, native per-token rule with the accepted state kept"}
+            "sample": f"{reps} passes over one full step of {s.name}: {s.layers} layers x "
+                      f"{len(real)} rows x {s.hv} heads, native per-token rule with the accepted "
+                      f"state kept"}
 
 
 def counters_traffic(commit_launch_bytes):
