@@ -18,6 +18,8 @@ GDN_MAX_LAYERS = 64
 GDN_HEAD_DIM = 128
 GDN_MAX_REC_TOKENS = 16
 GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
+GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
+OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_align_plan", "gdn_native_window",
@@ -45,9 +47,11 @@ class gdn_verify_io(C.Structure):
         ("q", C.c_void_p), ("q_tok_stride", C.c_int64), ("q_head_stride", C.c_int64),
         ("k", C.c_void_p), ("k_tok_stride", C.c_int64), ("k_head_stride", C.c_int64),
         ("v", C.c_void_p), ("v_tok_stride", C.c_int64), ("v_head_stride", C.c_int64),
-        ("a_log", C.c_void_p), ("beta", C.c_void_p), ("gate_tok_stride", C.c_int64),
+        ("a", C.c_void_p), ("b", C.c_void_p), ("gate_tok_stride", C.c_int64),
         ("out", C.c_void_p), ("out_tok_stride", C.c_int64), ("out_head_stride", C.c_int64),
-        ("num_tokens", C.c_int64), ("scale", C.c_float), ("reserved", C.c_int32),
+        ("num_tokens", C.c_int64), ("scale", C.c_float), ("gate_mode", C.c_int32),
+        ("A_log", C.c_void_p), ("dt_bias", C.c_void_p),
+        ("out_dtype", C.c_int32), ("reserved", C.c_int32),
     ]
 
 
@@ -154,30 +158,44 @@ class Pools:
                            dtype=torch.float32, device=device)
 
 
-def _io(q, k, v, a_log, beta, out, scale) -> gdn_verify_io:
+def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
             raise TypeError(f"{name} must be a bf16 [tokens][heads][128] view, feature-contiguous")
-    if a_log.dtype != torch.float32 or beta.dtype != torch.float32 or a_log.dim() != 2 \
-            or a_log.stride(1) != 1 or beta.stride() != a_log.stride():
-        raise TypeError("a_log and beta must be fp32 [tokens][HV] with the same strides")
-    if out.dtype != torch.float32 or out.dim() != 3 or out.stride(2) != 1:
-        raise TypeError("out must be an fp32 [tokens][HV][128] view, feature-contiguous")
+    if a.dtype != torch.float32 or b.dtype != torch.float32 or a.dim() != 2 \
+            or a.stride(1) != 1 or b.stride() != a.stride():
+        raise TypeError("a and b must be fp32 [tokens][HV] with the same strides")
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.dim() != 3 or out.stride(2) != 1:
+        raise TypeError("out must be an fp32 or bf16 [tokens][HV][128] view, feature-contiguous")
+    if (A_log is None) != (dt_bias is None):
+        raise TypeError("raw gates need both A_log and dt_bias")
     io = gdn_verify_io()
     io.q, io.q_tok_stride, io.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
     io.k, io.k_tok_stride, io.k_head_stride = k.data_ptr(), k.stride(0), k.stride(1)
     io.v, io.v_tok_stride, io.v_head_stride = v.data_ptr(), v.stride(0), v.stride(1)
-    io.a_log, io.beta, io.gate_tok_stride = a_log.data_ptr(), beta.data_ptr(), a_log.stride(0)
+    io.a, io.b, io.gate_tok_stride = a.data_ptr(), b.data_ptr(), a.stride(0)
     io.out, io.out_tok_stride, io.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
-    io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a_log.shape[0], out.shape[0])
+    io.out_dtype = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a.shape[0], out.shape[0])
     io.scale = float(scale)
+    io.gate_mode = GATE_LOG
+    if A_log is not None:
+        for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+            if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+                raise TypeError(f"{name} must be a contiguous fp32 [HV] tensor")
+        io.gate_mode = GATE_RAW
+        io.A_log, io.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
     return io
 
 
 def gdn_verify(pools: Pools, layer: int, state_slot, rec_slot, tok_start, win_len, rec_base,
-               q, k, v, a_log, beta, out, *, scale=1.0, err_flags=None, stream=None) -> int:
+               q, k, v, a, b, out, *, scale=1.0, A_log=None, dt_bias=None, err_flags=None,
+               stream=None) -> int:
+    """Verify one layer. a, b are the log-gate and write strength, or, with
+    A_log and dt_bias given, the raw gate projections (gates formed in the
+    kernel). out may be fp32 or bf16."""
     lib = load_library()
-    io = _io(q, k, v, a_log, beta, out, scale)
+    io = _io(q, k, v, a, b, out, scale, A_log, dt_bias)
     n = state_slot.shape[0]
     return _check(lib.gdn_verify(C.byref(pools.c), layer, n, _ptr(_i32(state_slot, "state_slot")),
                                  _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(tok_start, "tok_start")),
@@ -186,10 +204,10 @@ def gdn_verify(pools: Pools, layer: int, state_slot, rec_slot, tok_start, win_le
 
 
 def gdn_native_window(pools: Pools, layer: int, state_slot, tok_start, win_len,
-                      q, k, v, a_log, beta, out, snap, *, scale=1.0, err_flags=None,
-                      stream=None) -> int:
+                      q, k, v, a, b, out, snap, *, scale=1.0, A_log=None, dt_bias=None,
+                      err_flags=None, stream=None) -> int:
     lib = load_library()
-    io = _io(q, k, v, a_log, beta, out, scale)
+    io = _io(q, k, v, a, b, out, scale, A_log, dt_bias)
     if snap.dtype != pools.dtype or not snap.is_contiguous():
         raise TypeError("snap must be contiguous with the pool's dtype")
     n = state_slot.shape[0]

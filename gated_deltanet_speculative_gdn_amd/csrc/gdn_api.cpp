@@ -41,21 +41,27 @@ int32_t check_layer_ptrs(const gdn_pools* p, int32_t layer, bool need_rec)
 int32_t check_io(const gdn_verify_io* io)
 {
     if (!io) return GDN_ERR_NULL;
-    if (!io->q || !io->k || !io->v || !io->a_log || !io->beta || !io->out) return GDN_ERR_NULL;
+    if (!io->q || !io->k || !io->v || !io->a || !io->b || !io->out) return GDN_ERR_NULL;
+    if (io->gate_mode != GDN_GATE_LOG && io->gate_mode != GDN_GATE_RAW) return GDN_ERR_SHAPE;
+    if (io->out_dtype != GDN_OUT_F32 && io->out_dtype != GDN_OUT_BF16) return GDN_ERR_DTYPE;
+    if (io->gate_mode == GDN_GATE_RAW && (!io->A_log || !io->dt_bias)) return GDN_ERR_NULL;
     if (io->num_tokens < 0 || io->gate_tok_stride < 0) return GDN_ERR_SHAPE;
     if (io->q_tok_stride < 0 || io->q_head_stride < 0 || io->k_tok_stride < 0 ||
         io->k_head_stride < 0 || io->v_tok_stride < 0 || io->v_head_stride < 0 ||
         io->out_tok_stride < 0 || io->out_head_stride < 0)
         return GDN_ERR_SHAPE;
-    // 16-byte vector access: bf16 rows need strides in multiples of 8 elements,
-    // fp32 output rows multiples of 4.
-    if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v) || !aligned16(io->out))
+    // 16-byte vector access: bf16 input rows need strides in multiples of 8
+    // elements; output pieces are 4 elements (16 bytes fp32, 8 bytes bf16).
+    if (!aligned16(io->q) || !aligned16(io->k) || !aligned16(io->v)) return GDN_ERR_ALIGN;
+    if (io->out_dtype == GDN_OUT_F32 ? !aligned16(io->out) : ((uintptr_t)io->out & 7u) != 0)
         return GDN_ERR_ALIGN;
     if ((io->q_tok_stride | io->q_head_stride | io->k_tok_stride | io->k_head_stride |
          io->v_tok_stride | io->v_head_stride) & 7)
         return GDN_ERR_ALIGN;
     if ((io->out_tok_stride | io->out_head_stride) & 3) return GDN_ERR_ALIGN;
-    if (((uintptr_t)io->a_log & 3u) || ((uintptr_t)io->beta & 3u)) return GDN_ERR_ALIGN;
+    if (((uintptr_t)io->a & 3u) || ((uintptr_t)io->b & 3u)) return GDN_ERR_ALIGN;
+    if (io->gate_mode == GDN_GATE_RAW && (((uintptr_t)io->A_log & 3u) || ((uintptr_t)io->dt_bias & 3u)))
+        return GDN_ERR_ALIGN;
     return GDN_OK;
 }
 
@@ -64,8 +70,11 @@ void fill_io(VerifyParams& v, const gdn_verify_io* io)
     v.q = io->q; v.q_ts = io->q_tok_stride; v.q_hs = io->q_head_stride;
     v.k = io->k; v.k_ts = io->k_tok_stride; v.k_hs = io->k_head_stride;
     v.v = io->v; v.v_ts = io->v_tok_stride; v.v_hs = io->v_head_stride;
-    v.a_log = io->a_log; v.beta = io->beta; v.g_ts = io->gate_tok_stride;
+    v.a_log = io->a; v.beta = io->b; v.g_ts = io->gate_tok_stride;
+    v.raw_gates = io->gate_mode == GDN_GATE_RAW;
+    v.A_log = io->A_log; v.dt_bias = io->dt_bias;
     v.out = io->out; v.o_ts = io->out_tok_stride; v.o_hs = io->out_head_stride;
+    v.out_bf16 = io->out_dtype == GDN_OUT_BF16;
     v.num_tokens = io->num_tokens;
     v.scale = io->scale;
 }
@@ -90,7 +99,7 @@ const char* gdn_status_string(int32_t s)
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "a required pointer is NULL";
     case GDN_ERR_SHAPE: return "a size or index argument is out of range";
-    case GDN_ERR_DTYPE: return "unsupported state dtype";
+    case GDN_ERR_DTYPE: return "unsupported state or output dtype";
     case GDN_ERR_ALIGN: return "a pointer or stride breaks the 16-byte alignment rule";
     case GDN_ERR_LAUNCH: return "the HIP kernel launch failed";
     default: return "unknown status";

@@ -18,6 +18,7 @@ constexpr int kDim = 128;          // K = V = 128
 constexpr int kHeadElems = kDim * kDim;
 constexpr int kThreads = 256;      // four wave64s per workgroup
 constexpr float kNormEps = 1e-6f;  // inside the square root of the L2 norm
+constexpr float kSoftplusLinear = 20.f;  // softplus(x) = x above this input
 
 // Row-error bits, the values the C ABI documents.
 constexpr int kRowSlot = 1, kRowWin = 2, kRowN = 4, kRowBnd = 8, kRowTable = 16,

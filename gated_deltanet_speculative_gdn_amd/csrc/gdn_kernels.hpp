@@ -23,13 +23,16 @@ struct VerifyParams {
     const uint16_t* q; int64_t q_ts, q_hs;
     const uint16_t* k; int64_t k_ts, k_hs;
     const uint16_t* v; int64_t v_ts, v_hs;
-    const float* a_log; const float* beta; int64_t g_ts;
-    float* out; int64_t o_ts, o_hs;
+    const float* a_log; const float* beta; int64_t g_ts;   // log-gate and beta, or raw a and b
+    const float* A_log; const float* dt_bias;               // raw gates only: per value head
+    void* out; int64_t o_ts, o_hs;                          // fp32 or bf16 [tokens][HV][V]
     int64_t num_tokens;
     int64_t rec_stride;       // floats per (record slot, value head)
     int32_t* err;
     int32_t num_rows, hv, group, num_slots, num_rec_slots, T;
     float scale;
+    bool raw_gates;           // gates from raw a, b with A_log, dt_bias
+    bool out_bf16;            // outputs rounded to bf16 (nearest even)
 };
 
 // The all-layer commit.

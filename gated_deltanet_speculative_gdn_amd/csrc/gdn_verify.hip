@@ -276,9 +276,19 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             av = p.a_log[tok * p.g_ts + hv];
             bv = p.beta[tok * p.g_ts + hv];
         }
-        const float g = expf(av);
+        float g, be;
+        if (p.raw_gates) {
+            // g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+            const float x = av + p.dt_bias[hv];
+            const float sp = x > kSoftplusLinear ? x : log1pf(expf(x));
+            g = expf(-expf(p.A_log[hv]) * sp);
+            be = 1.0f / (1.0f + expf(-bv));
+        } else {
+            g = expf(av);
+            be = bv;
+        }
         L.g[j0 + t] = g;
-        L.be[j0 + t] = bv;
+        L.be[j0 + t] = be;
         if (!SNAP && lead) recb[2 * (int64_t)T * kDim + j0 + t] = g;
     }
     __syncthreads();
@@ -365,8 +375,13 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int i = tid; i < w * kRow4; i += NT) {
             const int t = i / kRow4;
             const int c = 4 * (i - t * kRow4);
-            st4(p.out + ((int64_t)ts + t) * p.o_ts + (int64_t)hv * p.o_hs + row0 + c,
-                ld4(L.ob + (j0 + t) * kDim + row0 + c));
+            const f32x4 ov = ld4(L.ob + (j0 + t) * kDim + row0 + c);
+            const int64_t oo = ((int64_t)ts + t) * p.o_ts + (int64_t)hv * p.o_hs + row0 + c;
+            if (p.out_bf16)
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) =
+                    u32x2{pack_bf16(ov.x, ov.y), pack_bf16(ov.z, ov.w)};
+            else
+                st4(static_cast<float*>(p.out) + oo, ov);
             if constexpr (!SNAP) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kDim + row0 + c));
         }
     }

@@ -214,6 +214,38 @@ def make_workload(spec: WorkloadSpec, device="cpu", state_dtype=torch.float32,
     return wl
 
 
+@dataclass
+class RawGates:
+    """Raw per-token gate projections of every layer and the per-head gate
+    parameters, for the raw-input gating variant of verify."""
+    a: torch.Tensor        # [L][tokens][HV] fp32
+    b: torch.Tensor        # [L][tokens][HV] fp32
+    A_log: torch.Tensor    # [L][HV] fp32
+    dt_bias: torch.Tensor  # [L][HV] fp32
+
+
+RAW_GATE_SEED_OFFSET = 7919
+
+
+def make_raw_gates(wl: Workload, device="cpu", seed: int | None = None) -> RawGates:
+    """Draw raw gate inputs for a workload from a stream of their own (the
+    workload's own draws are unchanged). a, b ~ N(0, 1); per head, A_log =
+    log A with A ~ U(1, 16) and dt_bias the inverse softplus of a time step
+    drawn log-uniform in [1e-3, 1e-1] (the initialisation recipe of Mamba-2
+    style decay parameters)."""
+    s = wl.spec
+    seed = (s.seed if seed is None else seed) + RAW_GATE_SEED_OFFSET
+    rng = np.random.default_rng(seed)
+    L, T, HV = s.layers, wl.tokens, s.hv
+    a = rng.standard_normal((L, T, HV)).astype(np.float32)
+    b = rng.standard_normal((L, T, HV)).astype(np.float32)
+    A_log = np.log(rng.uniform(1.0, 16.0, (L, HV))).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (L, HV)))
+    dt_bias = (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+    dev = torch.device(device)
+    return RawGates(*(torch.as_tensor(x, device=dev) for x in (a, b, A_log, dt_bias)))
+
+
 def acceptance_rate_counts(rng: np.random.Generator, rows: int,
                            rates=(0.856, 0.694, 0.558, 0.457, 0.376)) -> np.ndarray:
     """Accepted counts drawn from per-position acceptance rates (a draft token

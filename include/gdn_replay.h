@@ -26,7 +26,8 @@
  *
  * Per token t of one value head (K = V = 128, all fp32):
  *   k_hat = k / sqrt(|k|^2 + 1e-6),  q_tilde = scale * q / sqrt(|q|^2 + 1e-6)
- *   g = exp(a)  (a = log-gate),  h' = g * h
+ *   g = exp(a)  (a = log-gate; see gdn_verify_io for the raw-input gating),
+ *   h' = g * h
  *   delta = beta * (v - h' k_hat),  h = fma(delta, k_hat^T, h')
  *   o_t = h q_tilde
  * Value head hv reads key head hv / (HV / HK).
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 #define GDN_MAX_LAYERS 64      /* layers per pool set */
 #define GDN_HEAD_DIM 128       /* K = V = 128 */
 #define GDN_MAX_REC_TOKENS 16  /* record capacity T per row */
@@ -62,12 +63,14 @@ typedef enum {
     GDN_OK = 0,
     GDN_ERR_NULL = -1,    /* a required pointer is NULL */
     GDN_ERR_SHAPE = -2,   /* a size or index argument is out of range */
-    GDN_ERR_DTYPE = -3,   /* unsupported state dtype */
+    GDN_ERR_DTYPE = -3,   /* unsupported state or output dtype */
     GDN_ERR_ALIGN = -4,   /* a pointer or stride breaks the 16-byte rule */
     GDN_ERR_LAUNCH = -5   /* the HIP launch failed */
 } gdn_status;
 
 typedef enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 } gdn_state_dtype;
+typedef enum { GDN_GATE_LOG = 0, GDN_GATE_RAW = 1 } gdn_gate_mode;
+typedef enum { GDN_OUT_F32 = 0, GDN_OUT_BF16 = 1 } gdn_out_dtype;
 
 /* Device row-error bits (OR'ed into *err_flags). */
 enum {
@@ -110,13 +113,25 @@ typedef struct gdn_pools {
 
 /*
  * Per-token inputs and outputs of one layer's verify ([vLLM] Commits item 2:
- * strided q/k/v views of the short-conv output, output written in place).
- * Strides are in elements; the innermost (feature) dimension is contiguous.
+ * the verify reads strided q/k/v views of the short-conv output and writes
+ * straight into the layer output). Strides are in elements; the innermost
+ * (feature) dimension is contiguous.
  *   q, k: device bf16 bits, [tokens][HK][K];  v: device bf16 bits, [tokens][HV][V].
  *     Base pointers 16-byte aligned, strides multiples of 8 elements.
- *   a_log, beta: device fp32 [tokens][HV] (head stride 1); a_log is the
- *     log-gate (the decay is exp(a_log)), beta the write strength.
- *   out: device fp32 [tokens][HV][V]; 16-byte aligned, strides multiples of 4.
+ *   a, b: device fp32 [tokens][HV] (head stride 1, token stride gate_tok_stride).
+ *     gate_mode GDN_GATE_LOG: a is the log-gate (decay g = exp(a)) and b the
+ *       write strength beta.
+ *     gate_mode GDN_GATE_RAW: a and b are the layer's raw gate projections and
+ *       the gates are formed in the kernel with the per-head parameters
+ *       A_log, dt_bias (device fp32 [HV], 4-byte aligned):
+ *         g = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])),  beta = sigmoid(b),
+ *       softplus(x) = x for x > 20, else log(1 + exp(x)). This parameterisation
+ *       is not printed on the pages; it is the decay/write-strength form used
+ *       with Gated DeltaNet layers ([GDN]).
+ *     Either way the record holds the decay g that was multiplied in.
+ *   out: device [tokens][HV][V], fp32 (out_dtype GDN_OUT_F32; 16-byte aligned,
+ *     strides multiples of 4) or bf16 bits rounded to nearest even once
+ *     (GDN_OUT_BF16; 8-byte aligned, strides multiples of 4).
  *   num_tokens: rows address tokens [tok_start, tok_start + w) < num_tokens.
  *   scale: multiplies the normalised query (1 = the plain o_t = S_t q_t).
  */
@@ -124,11 +139,15 @@ typedef struct gdn_verify_io {
     const uint16_t* q;  int64_t q_tok_stride, q_head_stride;
     const uint16_t* k;  int64_t k_tok_stride, k_head_stride;
     const uint16_t* v;  int64_t v_tok_stride, v_head_stride;
-    const float* a_log; const float* beta; int64_t gate_tok_stride;
-    float* out;         int64_t out_tok_stride, out_head_stride;
+    const float* a;     const float* b;  int64_t gate_tok_stride;
+    void* out;          int64_t out_tok_stride, out_head_stride;
     int64_t num_tokens;
     float scale;
-    int32_t reserved;   /* set to 0 */
+    int32_t gate_mode;      /* gdn_gate_mode */
+    const float* A_log;     /* GDN_GATE_RAW only, else ignored */
+    const float* dt_bias;   /* GDN_GATE_RAW only, else ignored */
+    int32_t out_dtype;      /* gdn_out_dtype */
+    int32_t reserved;       /* set to 0 */
 } gdn_verify_io;
 
 /*

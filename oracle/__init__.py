@@ -71,6 +71,10 @@ def _load():
             fn.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int,
                            rp, i32p, rp, rp, rp, rp, rp, rc, rc,
                            rp, rp, rp, rp, vp, vp, vp, C.c_int, C.c_int]
+        for suf, rp in (("f32", f32p), ("f64", f64p)):
+            fn = getattr(lib, f"gdno_raw_gates_{suf}")
+            fn.restype = C.c_int
+            fn.argtypes = [C.c_long, C.c_int, rp, rp, rp, rp, rp, rp]
         lib.gdno_replay_heads_f32.restype = C.c_int
         lib.gdno_replay_heads_f32.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, f32p, i32p,
                                               f32p, f32p, f32p, C.c_int]
@@ -165,6 +169,26 @@ def replay_heads(S, n, rec_delta, rec_khat, rec_g, *, nthreads=None) -> np.ndarr
     if rc != 0:
         raise ValueError("oracle replay_heads rejected its arguments")
     return S
+
+
+def raw_gates(a, b, A_log, dt_bias, *, dtype=np.float32):
+    """Log-gate and write strength from raw per-token inputs a, b [..., HV]
+    with per-head A_log, dt_bias [HV]: log-gate = -exp(A_log) softplus(a +
+    dt_bias) (softplus linear above 20), beta = sigmoid(b). Returns
+    (log_gate, beta) shaped like a."""
+    lib = _load()
+    a = _c(a, dtype)
+    b = _c(b, dtype)
+    hv = a.shape[-1]
+    if b.shape != a.shape or np.shape(A_log) != (hv,) or np.shape(dt_bias) != (hv,):
+        raise ValueError("a, b [..., HV] and A_log, dt_bias [HV]")
+    lg = np.empty_like(a)
+    be = np.empty_like(a)
+    fn = lib.gdno_raw_gates_f32 if dtype == np.float32 else lib.gdno_raw_gates_f64
+    if fn(a.size, hv, a.reshape(-1), b.reshape(-1), _c(A_log, dtype), _c(dt_bias, dtype),
+          lg.reshape(-1), be.reshape(-1)) != 0:
+        raise ValueError("raw_gates: bad argument")
+    return lg, be
 
 
 def bf16_to_f32(bits) -> np.ndarray:

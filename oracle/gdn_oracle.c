@@ -39,24 +39,28 @@
 #define FMA fmaf
 #define SQRT sqrtf
 #define EXP expf
+#define LOG1P log1pf
 #include "gdn_oracle_body.h"
 #undef REAL
 #undef SUFFIX
 #undef FMA
 #undef SQRT
 #undef EXP
+#undef LOG1P
 
 #define REAL double
 #define SUFFIX f64
 #define FMA fma
 #define SQRT sqrt
 #define EXP exp
+#define LOG1P log1p
 #include "gdn_oracle_body.h"
 #undef REAL
 #undef SUFFIX
 #undef FMA
 #undef SQRT
 #undef EXP
+#undef LOG1P
 
 int gdno_version(void) { return 1; }
 
@@ -127,6 +131,24 @@ int gdno_native_heads_##SUF(int nheads, int K, int V, int T,                    
 
 BATCH_NATIVE(f32, float)
 BATCH_NATIVE(f64, double)
+
+/* Gates from raw inputs for n (token, value head) entries laid out
+ * [tokens][HV] (head fastest): entry i uses A_log[i % hv], dt_bias[i % hv].
+ * Writes the log-gate (the decay is exp of it) and beta. Return 0, or -1 on
+ * a bad argument. */
+#define BATCH_RAW_GATES(SUF, R)                                                        \
+int gdno_raw_gates_##SUF(long n, int hv, const R* a, const R* b, const R* A_log,        \
+                         const R* dt_bias, R* log_gate, R* beta)                        \
+{                                                                                       \
+    if (n < 0 || hv < 1) return -1;                                                     \
+    for (long i = 0; i < n; ++i)                                                        \
+        raw_gate_##SUF(a[i], b[i], A_log[i % hv], dt_bias[i % hv], log_gate + i,        \
+                       beta + i);                                                       \
+    return 0;                                                                           \
+}
+
+BATCH_RAW_GATES(f32, float)
+BATCH_RAW_GATES(f64, double)
 
 /* Replay n[i] recorded tokens of head i onto S[i] in place ([vLLM] Test
  * Result: h = fma(correction, key, h * decay), token by token). */

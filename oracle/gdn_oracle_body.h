@@ -4,7 +4,7 @@
  * TEST INFRASTRUCTURE. Included twice by gdn_oracle.c: once with REAL = float
  * (the reference every GPU result is compared with) and once with
  * REAL = double (used only to bound the float version's own rounding error).
- * The caller defines REAL, SUFFIX, FMA, SQRT and EXP before including it.
+ * The caller defines REAL, SUFFIX, FMA, SQRT, EXP and LOG1P before including it.
  *
  * Sources, cited by page title and section:
  *   [GDN]  Yang, Kautz, Hatamizadeh, "Gated Delta Networks: Improving Mamba2
@@ -108,6 +108,25 @@ static void GLUE(replay_head_, SUFFIX)(
                 h[(long)v * K + kk] = FMA(d[v], kh[kk], decayed);
             }
     }
+}
+
+
+/* Gates from the raw per-token projections a, b of one value head with that
+ * head's parameters A_log, dt_bias. The pages give no formula for this step;
+ * the reading taken is the decay parameterisation used with Gated DeltaNet
+ * layers [GDN]:
+ *   x = a + dt_bias,  softplus(x) = x if x > 20, else log(1 + exp(x))
+ *   log-gate = -exp(A_log) * softplus(x)      (the decay is exp(log-gate))
+ *   beta     = 1 / (1 + exp(-b))
+ * One IEEE operation per step, in the order written. */
+static void GLUE(raw_gate_, SUFFIX)(REAL a, REAL b, REAL A_log, REAL dt_bias,
+                                    REAL* log_gate, REAL* beta)
+{
+    REAL x = a + dt_bias;
+    REAL sp = x > (REAL)20 ? x : LOG1P(EXP(x));
+    REAL rate = EXP(A_log);
+    *log_gate = -(rate * sp);
+    *beta = (REAL)1 / ((REAL)1 + EXP(-b));
 }
 
 #undef GLUE

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.gdn_status_string(s), bytes)
     assert lib.gdn_status_string(-4).decode().startswith("a pointer or stride")
@@ -71,7 +71,7 @@ def good_io():
     io.q, io.q_tok_stride, io.q_head_stride = 0x30000, 512, 128
     io.k, io.k_tok_stride, io.k_head_stride = 0x40000, 512, 128
     io.v, io.v_tok_stride, io.v_head_stride = 0x50000, 512, 128
-    io.a_log, io.beta, io.gate_tok_stride = 0x60000, 0x70000, 4
+    io.a, io.b, io.gate_tok_stride = 0x60000, 0x70000, 4
     io.out, io.out_tok_stride, io.out_head_stride = 0x80000, 512, 128
     io.num_tokens, io.scale = 16, 1.0
     return io
@@ -108,7 +108,14 @@ def test_verify_zero_rows_is_ok_without_launch(lib):
     (lambda p, io: setattr(io, "q", 0x30008), E_ALIGN),
     (lambda p, io: setattr(io, "k_tok_stride", 516), E_ALIGN),
     (lambda p, io: setattr(io, "out_head_stride", 130), E_ALIGN),
-    (lambda p, io: setattr(io, "a_log", 0x60002), E_ALIGN),
+    (lambda p, io: setattr(io, "a", 0x60002), E_ALIGN),
+    (lambda p, io: setattr(io, "gate_mode", 2), E_SHAPE),
+    (lambda p, io: setattr(io, "out_dtype", 2), E_DTYPE),
+    (lambda p, io: setattr(io, "gate_mode", 1), E_NULL),                  # raw gates, no A_log
+    (lambda p, io: (setattr(io, "gate_mode", 1), setattr(io, "A_log", 0x90000),
+                    setattr(io, "dt_bias", 0x90102)), E_ALIGN),
+    (lambda p, io: (setattr(io, "out_dtype", 1), setattr(io, "out", 0x80004)), E_ALIGN),
+    (lambda p, io: setattr(io, "out", 0x80008), E_ALIGN),                 # fp32 out: 16-byte rule
     (lambda p, io: setattr(io, "num_tokens", -1), E_SHAPE),
     (lambda p, io: setattr(io, "v_head_stride", -8), E_SHAPE),
 ])
@@ -120,6 +127,13 @@ def test_verify_rejects_malformed(lib, mutate, status):
         assert verify(lib, p, io, rows=0) == OK
         return
     assert verify(lib, p, io) == status
+
+
+def test_verify_accepts_raw_gates_and_bf16_out(lib):
+    io = good_io()
+    io.gate_mode, io.A_log, io.dt_bias = 1, 0x90000, 0x90100
+    io.out_dtype, io.out = 1, 0x80008          # bf16 output: 8-byte pieces
+    assert verify(lib, good_pools(), io, rows=0) == OK
 
 
 def test_verify_rejects_bad_layer_and_rows(lib):

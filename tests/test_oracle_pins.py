@@ -357,3 +357,64 @@ def test_align_plan_errors():
     t2 = np.array([[1, 2, 3, 4]], np.int32)
     _, _, _, _, err2 = oracle.align_plan([3], [9], t2, 4, 16)
     assert err2.tolist() == [8]
+
+
+# ---- gates from raw inputs ---------------------------------------------------
+# Reading (the pages print no formula for this step): log-gate =
+# -exp(A_log) softplus(a + dt_bias) with softplus linear above 20, beta =
+# sigmoid(b). The pins below fix that formula's pieces by closed forms,
+# identities and the library's own softplus / sigmoid.
+
+def test_raw_gates_closed_forms():
+    # softplus(0) = ln 2 and exp(0) = 1: log-gate -ln 2, decay exactly 1/2 in fp64
+    lg, be = oracle.raw_gates([[0.0]], [[0.0]], [0.0], [0.0], dtype=np.float64)
+    assert lg[0, 0] == pytest.approx(-np.log(2.0), rel=1e-15, abs=0)
+    assert be[0, 0] == 0.5
+    # linear branch: a + dt_bias = 25 > 20 gives softplus = 25; A_log = ln 3 gives rate 3
+    lg, _ = oracle.raw_gates([[20.0]], [[0.0]], [np.log(3.0)], [5.0], dtype=np.float64)
+    assert lg[0, 0] == pytest.approx(-75.0, rel=1e-14)
+    # the split point itself stays on the log branch: softplus(20) = 20 + log1p(e^-20)
+    lg, _ = oracle.raw_gates([[20.0]], [[0.0]], [0.0], [0.0], dtype=np.float64)
+    assert lg[0, 0] == pytest.approx(-(20.0 + np.log1p(np.exp(-20.0))), rel=1e-15)
+
+
+def test_raw_gates_identities_and_library_forms():
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-19.0, 19.0, (64, 1))
+    b = rng.normal(0, 3, (64, 1))
+    zero = np.zeros(1)
+    lg_p, be_p = oracle.raw_gates(x, b, zero, zero, dtype=np.float64)
+    lg_m, be_m = oracle.raw_gates(-x, -b, zero, zero, dtype=np.float64)
+    # softplus(x) - softplus(-x) = x; sigmoid(b) + sigmoid(-b) = 1
+    np.testing.assert_allclose(lg_m - lg_p, x, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(be_p + be_m, 1.0, rtol=0, atol=1e-15)
+    # library forms: softplus(x) = logaddexp(0, x), sigmoid = 1 / (1 + exp(-b))
+    np.testing.assert_allclose(-lg_p, np.logaddexp(0.0, x), rtol=1e-14)
+    import scipy.special
+    np.testing.assert_allclose(be_p, scipy.special.expit(b), rtol=1e-14)
+
+
+def test_raw_gates_per_head_parameters():
+    """Entry i uses the parameters of head i % HV: rates 1, 2, 4 scale the
+    log-gate of heads 0, 1, 2, and dt_bias shifts the input of its own head."""
+    a = np.full((3, 3), 0.5)
+    A_log = np.log([1.0, 2.0, 4.0])
+    lg, _ = oracle.raw_gates(a, np.zeros((3, 3)), A_log, np.zeros(3), dtype=np.float64)
+    sp = np.logaddexp(0.0, 0.5)
+    np.testing.assert_allclose(lg, -np.array([[1.0, 2.0, 4.0]] * 3) * sp, rtol=1e-14)
+    lg, _ = oracle.raw_gates(np.zeros((2, 3)), np.zeros((2, 3)), np.zeros(3),
+                             np.array([0.0, 1.0, -1.0]), dtype=np.float64)
+    np.testing.assert_allclose(lg, -np.logaddexp(0.0, np.array([[0.0, 1.0, -1.0]] * 2)),
+                               rtol=1e-14)
+
+
+def test_raw_gates_fp32_close_to_fp64():
+    rng = np.random.default_rng(6)
+    a = rng.normal(size=(32, 8)).astype(F32)
+    b = rng.normal(size=(32, 8)).astype(F32)
+    A_log = np.log(rng.uniform(1, 16, 8)).astype(F32)
+    dtb = rng.normal(-4, 1, 8).astype(F32)
+    lg32, be32 = oracle.raw_gates(a, b, A_log, dtb)
+    lg64, be64 = oracle.raw_gates(a, b, A_log, dtb, dtype=np.float64)
+    np.testing.assert_allclose(lg32, lg64, rtol=4e-7)
+    np.testing.assert_allclose(be32, be64, rtol=4e-7)
