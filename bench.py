@@ -59,12 +59,13 @@ def i32(x):
 class Step:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, raw_gates=False, out_dtype=torch.float32):
         s = wl.spec
         self.wl, self.s = wl, s
         self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens)
         self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens)
-        self.out = torch.zeros((s.layers, wl.tokens, s.hv, s.dv), device="cuda")
+        self.out = torch.zeros((s.layers, wl.tokens, s.hv, s.dv), dtype=out_dtype, device="cuda")
+        self.rg = W.make_raw_gates(wl, device="cuda") if raw_gates else None
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.slot = i32(wl.state_slot)
         self.rec_slot = i32(wl.rec_slot)
@@ -73,12 +74,21 @@ class Step:
         self.n = i32(wl.n_accept)
         self.snaps = None
 
+    def gates(self, layer):
+        """(a, b, keyword arguments) of the layer's verify: log-gate and beta,
+        or the raw projections with the per-head gate parameters."""
+        if self.rg is None:
+            return self.wl.a[layer], self.wl.beta[layer], {}
+        rg = self.rg
+        return rg.a[layer], rg.b[layer], {"A_log": rg.A_log[layer], "dt_bias": rg.dt_bias[layer]}
+
     def verify_all(self):
         wl = self.wl
         for layer in range(self.s.layers):
+            a, b, kw = self.gates(layer)
             G.gdn_verify(self.pools, layer, self.slot, self.rec_slot, self.tok, self.win, None,
-                         wl.q(layer), wl.k(layer), wl.v(layer), wl.a[layer], wl.beta[layer],
-                         self.out[layer], err_flags=self.err)
+                         wl.q(layer), wl.k(layer), wl.v(layer), a, b, self.out[layer],
+                         err_flags=self.err, **kw)
 
     def commit(self):
         G.gdn_commit_all_layers(self.pools, self.slot, self.slot, self.rec_slot, self.n,
@@ -91,16 +101,18 @@ class Step:
                                       dtype=wl.state_dtype, device="cuda")
                           for _ in range(s.layers)]
         for layer in range(s.layers):
+            a, b, kw = self.gates(layer)
             G.gdn_native_window(self.pools, layer, self.slot, self.tok, self.win, wl.q(layer),
-                                wl.k(layer), wl.v(layer), wl.a[layer], wl.beta[layer],
-                                self.out[layer], self.snaps[layer], err_flags=self.err)
+                                wl.k(layer), wl.v(layer), a, b, self.out[layer],
+                                self.snaps[layer], err_flags=self.err, **kw)
 
     def native_accept(self):
         G.gdn_native_accept(self.pools, self.snaps, self.slot, self.n, err_flags=self.err)
 
 
-def accounting(wl):
-    """Update counts and algorithmic HBM bytes of one step."""
+def accounting(wl, out_bytes=4, raw_gates=False):
+    """Update counts and algorithmic HBM bytes of one step (out_bytes: bytes
+    per output element; raw gates add the per-head parameters)."""
     s = wl.spec
     sb = 128 * 128 * (4 if wl.state_dtype == torch.float32 else 2)
     real = (wl.state_slot >= 0) & (wl.win_len > 0)
@@ -108,8 +120,8 @@ def accounting(wl):
     n = wl.n_accept[real].astype(np.int64)
     verify_updates = int(s.layers * s.hv * w.sum())
     commit_updates = int(s.layers * s.hv * n.sum())
-    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * 4 + REC_TOKEN_BYTES)
-    verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok)
+    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + REC_TOKEN_BYTES)
+    verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok + (s.hv * 8 if raw_gates else 0))
     commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * REC_TOKEN_BYTES))
     native_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * (per_tok - s.hv * REC_TOKEN_BYTES)
                              + w.sum() * s.hv * sb)
@@ -202,6 +214,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.MTP_B64.name, choices=sorted(W.WORKLOADS))
     ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--gating", default="log", choices=["log", "raw"],
+                    help="log: log-gate and beta given; raw: gates formed in the kernel from "
+                         "raw a, b with per-head A_log, dt_bias")
+    ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -220,8 +236,10 @@ def main():
     dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
     log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
     wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
-    acc = accounting(wl)
-    st = Step(wl)
+    acc = accounting(wl, out_bytes=2 if args.out_dtype == "bf16" else 4,
+                     raw_gates=args.gating == "raw")
+    st = Step(wl, raw_gates=args.gating == "raw",
+              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32)
     L = spec.layers
 
     # warm-up (also loads the code object before capture)
@@ -262,6 +280,7 @@ def main():
         "config": {"workload": spec.name, "layers": L, "batch": spec.rows,
                    "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
+                   "gating": args.gating, "out_dtype": args.out_dtype,
                    "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
         "roofline": {"bound": "hbm", "kernel": "commit_all_layers",
                      "achieved": com_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -203,6 +203,9 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     const int64_t gtok = (int64_t)ts + (tid < w ? tid : w - 1);
     const float a_in = p.a_log[gtok * p.g_ts + hv];
     const float b_in = p.beta[gtok * p.g_ts + hv];
+    // per-head gate parameters (raw gates); otherwise a harmless in-bounds read
+    const float alog_in = (p.raw_gates ? p.A_log : p.a_log)[hv];
+    const float dtb_in = (p.raw_gates ? p.dt_bias : p.beta)[hv];
     float* recb = nullptr;
     f32x4 ring_d[2], ring_k[2];
     float ring_g = 0.f;
@@ -279,9 +282,9 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         float g, be;
         if (p.raw_gates) {
             // g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
-            const float x = av + p.dt_bias[hv];
+            const float x = av + dtb_in;
             const float sp = x > kSoftplusLinear ? x : log1pf(expf(x));
-            g = expf(-expf(p.A_log[hv]) * sp);
+            g = expf(-expf(alog_in) * sp);
             be = 1.0f / (1.0f + expf(-bv));
         } else {
             g = expf(av);
