@@ -59,13 +59,14 @@ def i32(x):
 class Step:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, wl, raw_gates=False, out_dtype=torch.float32):
+    def __init__(self, wl, raw_gates=False, out_dtype=torch.float32, conv=None):
         s = wl.spec
         self.wl, self.s = wl, s
         self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens)
         self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens)
         self.out = torch.zeros((s.layers, wl.tokens, s.hv, s.dv), dtype=out_dtype, device="cuda")
         self.rg = W.make_raw_gates(wl, device="cuda") if raw_gates else None
+        self.conv = G.ConvPools(conv.state, conv.x) if conv is not None else None
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.slot = i32(wl.state_slot)
         self.rec_slot = i32(wl.rec_slot)
@@ -91,8 +92,13 @@ class Step:
                          err_flags=self.err, **kw)
 
     def commit(self):
-        G.gdn_commit_all_layers(self.pools, self.slot, self.slot, self.rec_slot, self.n,
-                                err_flags=self.err)
+        if self.conv is None:
+            G.gdn_commit_all_layers(self.pools, self.slot, self.slot, self.rec_slot, self.n,
+                                    err_flags=self.err)
+        else:
+            G.gdn_commit_all_layers_conv(self.pools, self.conv, self.slot, self.slot,
+                                         self.rec_slot, self.n, conv_tok_start=self.tok,
+                                         err_flags=self.err)
 
     def native_all(self):
         wl, s = self.wl, self.s
@@ -110,9 +116,10 @@ class Step:
         G.gdn_native_accept(self.pools, self.snaps, self.slot, self.n, err_flags=self.err)
 
 
-def accounting(wl, out_bytes=4, raw_gates=False):
+def accounting(wl, out_bytes=4, raw_gates=False, conv=None):
     """Update counts and algorithmic HBM bytes of one step (out_bytes: bytes
-    per output element; raw gates add the per-head parameters)."""
+    per output element; raw gates add the per-head parameters; conv: the
+    short-conv states compacted in the commit launch)."""
     s = wl.spec
     sb = 128 * 128 * (4 if wl.state_dtype == torch.float32 else 2)
     real = (wl.state_slot >= 0) & (wl.win_len > 0)
@@ -123,6 +130,11 @@ def accounting(wl, out_bytes=4, raw_gates=False):
     per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + REC_TOKEN_BYTES)
     verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok + (s.hv * 8 if raw_gates else 0))
     commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * REC_TOKEN_BYTES))
+    if conv is not None:
+        Ls, C = conv.state.shape[2], conv.state.shape[3]
+        row = C * conv.state.element_size()
+        # per live row and layer: read L_s state rows and n inputs, write L_s rows
+        commit_bytes += int(s.layers * ((n > 0).sum() * 2 * Ls * row + n.sum() * row))
     native_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * (per_tok - s.hv * REC_TOKEN_BYTES)
                              + w.sum() * s.hv * sb)
     accept_bytes = int(s.layers * s.hv * (n > 0).sum() * 2 * sb)
@@ -218,6 +230,9 @@ def main():
                     help="log: log-gate and beta given; raw: gates formed in the kernel from "
                          "raw a, b with per-head A_log, dt_bias")
     ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--conv", action="store_true",
+                    help="also compact bf16 short-conv states (width-4 conv over the mixed "
+                         "q/k/v channels) in the commit launch")
     ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -236,10 +251,11 @@ def main():
     dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
     log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
     wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    conv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if args.conv else None
     acc = accounting(wl, out_bytes=2 if args.out_dtype == "bf16" else 4,
-                     raw_gates=args.gating == "raw")
+                     raw_gates=args.gating == "raw", conv=conv)
     st = Step(wl, raw_gates=args.gating == "raw",
-              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32)
+              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32, conv=conv)
     L = spec.layers
 
     # warm-up (also loads the code object before capture)
@@ -280,7 +296,7 @@ def main():
         "config": {"workload": spec.name, "layers": L, "batch": spec.rows,
                    "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
-                   "gating": args.gating, "out_dtype": args.out_dtype,
+                   "gating": args.gating, "out_dtype": args.out_dtype, "conv_states": args.conv,
                    "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
         "roofline": {"bound": "hbm", "kernel": "commit_all_layers",
                      "achieved": com_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -22,8 +22,9 @@ GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
 OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
 
-EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_align_plan", "gdn_native_window",
-           "gdn_native_accept", "gdn_rec_stride", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv", "gdn_align_plan",
+           "gdn_native_window", "gdn_native_accept", "gdn_rec_stride", "gdn_status_string",
+           "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -39,6 +40,15 @@ class gdn_pools(C.Structure):
         ("num_state_slots", C.c_int32), ("num_rec_slots", C.c_int32),
         ("rec_tokens", C.c_int32), ("reserved", C.c_int32),
         ("state", C.c_void_p * GDN_MAX_LAYERS), ("rec", C.c_void_p * GDN_MAX_LAYERS),
+    ]
+
+
+class gdn_conv_pools(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32), ("channels", C.c_int32), ("state_len", C.c_int32),
+        ("dtype", C.c_int32), ("num_slots", C.c_int32), ("reserved", C.c_int32),
+        ("x_tok_stride", C.c_int64), ("num_tokens", C.c_int64),
+        ("state", C.c_void_p * GDN_MAX_LAYERS), ("x", C.c_void_p * GDN_MAX_LAYERS),
     ]
 
 
@@ -71,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     lib.gdn_verify.argtypes = [P(gdn_pools), i32, i32, vp, vp, vp, vp, vp, P(gdn_verify_io), vp, vp]
     lib.gdn_commit_all_layers.argtypes = [P(gdn_pools), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_commit_all_layers_conv.argtypes = [P(gdn_pools), P(gdn_conv_pools), i32, vp, vp, vp,
+                                               vp, vp, vp, vp, vp, vp]
     lib.gdn_align_plan.argtypes = [i32, vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.gdn_native_window.argtypes = [P(gdn_pools), i32, i32, vp, vp, vp, P(gdn_verify_io), vp,
                                       vp, vp]
@@ -158,6 +170,37 @@ class Pools:
                            dtype=torch.float32, device=device)
 
 
+class ConvPools:
+    """Short-conv state pools and this step's conv inputs (torch tensors,
+    caller-owned). state: [L][slots][state_len][C]; x: [L][tokens][>= C]
+    (channels contiguous), same dtype (fp32 or bf16)."""
+
+    def __init__(self, state, x):
+        self.state = list(state) if not torch.is_tensor(state) else [state[i] for i in range(state.shape[0])]
+        self.x = list(x) if not torch.is_tensor(x) else [x[i] for i in range(x.shape[0])]
+        s0, x0 = self.state[0], self.x[0]
+        self.num_slots, self.state_len, self.channels = s0.shape
+        self.dtype = s0.dtype
+        if self.dtype not in (torch.float32, torch.bfloat16) or x0.dtype != self.dtype:
+            raise TypeError("conv states and inputs share one dtype, fp32 or bf16")
+        if x0.dim() != 2 or x0.stride(1) != 1 or x0.shape[1] < self.channels:
+            raise TypeError("conv inputs are [tokens][>= C], channels contiguous")
+        st = gdn_conv_pools()
+        st.num_layers = len(self.state)
+        st.channels = self.channels
+        st.state_len = self.state_len
+        st.dtype = GDN_STATE_BF16 if self.dtype == torch.bfloat16 else GDN_STATE_F32
+        st.num_slots = self.num_slots
+        st.x_tok_stride = x0.stride(0)
+        st.num_tokens = x0.shape[0]
+        for i, (s_, x_) in enumerate(zip(self.state, self.x)):
+            if not s_.is_contiguous() or x_.stride() != x0.stride() or x_.shape != x0.shape:
+                raise TypeError("conv pools contiguous, conv inputs of one shape and stride")
+            st.state[i] = s_.data_ptr()
+            st.x[i] = x_.data_ptr()
+        self.c = st
+
+
 def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
@@ -227,6 +270,23 @@ def gdn_commit_all_layers(pools: Pools, src_slot, dst_slot, rec_slot, n_accept, 
         _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
         _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
         _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_commit_all_layers_conv(pools, conv, src_slot, dst_slot, rec_slot, n_accept,
+                               bnd_len=None, bnd_slot=None, conv_tok_start=None, *,
+                               err_flags=None, stream=None) -> int:
+    """The all-layer commit of the state pools (or None) together with the
+    short-conv state compaction of ``conv`` (a ConvPools, or None), one launch."""
+    lib = load_library()
+    n = src_slot.shape[0]
+    return _check(lib.gdn_commit_all_layers_conv(
+        C.byref(pools.c) if pools is not None else None,
+        C.byref(conv.c) if conv is not None else None, n,
+        _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
+        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
+        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
+        _ptr(_i32(conv_tok_start, "conv_tok_start")), _ptr(_i32(err_flags, "err_flags")),
+        _stream(stream)))
 
 
 def gdn_native_accept(pools: Pools, snaps, dst_slot, n_accept, *, err_flags=None,

@@ -65,6 +65,26 @@ int32_t check_io(const gdn_verify_io* io)
     return GDN_OK;
 }
 
+int64_t conv_elem_bytes(const gdn_conv_pools* c) { return c->dtype == GDN_STATE_BF16 ? 2 : 4; }
+int64_t conv_row_bytes(const gdn_conv_pools* c) { return (int64_t)c->channels * conv_elem_bytes(c); }
+
+int32_t check_conv(const gdn_conv_pools* c)
+{
+    if (c->num_layers < 1 || c->num_layers > GDN_MAX_LAYERS) return GDN_ERR_SHAPE;
+    if (c->dtype != GDN_STATE_F32 && c->dtype != GDN_STATE_BF16) return GDN_ERR_DTYPE;
+    if (c->channels < 1 || c->state_len < 1 || c->state_len > GDN_MAX_CONV_STATE ||
+        c->num_slots < 1 || c->num_tokens < 0 || c->x_tok_stride < c->channels)
+        return GDN_ERR_SHAPE;
+    if ((int64_t)c->channels * conv_elem_bytes(c) / 16 > INT32_MAX) return GDN_ERR_SHAPE;
+    if ((conv_row_bytes(c) & 15) || ((c->x_tok_stride * conv_elem_bytes(c)) & 15))
+        return GDN_ERR_ALIGN;
+    for (int32_t l = 0; l < c->num_layers; ++l) {
+        if (!c->state[l] || !c->x[l]) return GDN_ERR_NULL;
+        if (!aligned16(c->state[l]) || !aligned16(c->x[l])) return GDN_ERR_ALIGN;
+    }
+    return GDN_OK;
+}
+
 void fill_io(VerifyParams& v, const gdn_verify_io* io)
 {
     v.q = io->q; v.q_ts = io->q_tok_stride; v.q_hs = io->q_head_stride;
@@ -176,45 +196,92 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
         launch_native_window(v, pools->state_dtype == GDN_STATE_BF16, (hipStream_t)stream));
 }
 
+int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools* conv,
+                                   int32_t num_rows, const int32_t* src_slot,
+                                   const int32_t* dst_slot, const int32_t* rec_slot,
+                                   const int32_t* n_accept, const int32_t* bnd_len,
+                                   const int32_t* bnd_slot, const int32_t* conv_tok_start,
+                                   int32_t* err_flags, void* stream)
+{
+    int32_t st;
+    if (!pools && !conv) return GDN_ERR_NULL;
+    if (pools) {
+        if ((st = check_pools(pools))) return st;
+        for (int32_t l = 0; l < pools->num_layers; ++l)
+            if ((st = check_layer_ptrs(pools, l, true))) return st;
+        if (!rec_slot) return GDN_ERR_NULL;
+    }
+    if (conv) {
+        if ((st = check_conv(conv))) return st;
+        if (pools && conv->num_layers != pools->num_layers) return GDN_ERR_SHAPE;
+        if (!conv_tok_start) return GDN_ERR_NULL;
+    }
+    if (num_rows < 0) return GDN_ERR_SHAPE;
+    const int32_t layers = pools ? pools->num_layers : conv->num_layers;
+    int64_t wgs = 0;
+    if (pools) wgs += (int64_t)num_rows * pools->num_v_heads * layers * 8;
+    int64_t conv_per_row = 0;
+    if (conv) {
+        const int64_t pieces = conv_row_bytes(conv) / 16;
+        conv_per_row = (pieces + kConvPiecesPerWg - 1) / kConvPiecesPerWg;
+        wgs += (int64_t)num_rows * layers * conv_per_row;
+    }
+    if (wgs > INT32_MAX) return GDN_ERR_SHAPE;
+    if (!src_slot || !dst_slot || !n_accept) return GDN_ERR_NULL;
+    if ((bnd_len == nullptr) != (bnd_slot == nullptr)) return GDN_ERR_NULL;
+    if (num_rows == 0) return GDN_OK;
+
+    CommitParams c;
+    memset(&c, 0, sizeof(c));
+    c.src = src_slot;
+    c.dst = dst_slot;
+    c.n = n_accept;
+    c.bnd_len = bnd_len;
+    c.bnd_slot = bnd_slot;
+    c.err = err_flags;
+    c.num_layers = layers;
+    c.num_rows = num_rows;
+    if (pools) {
+        for (int32_t l = 0; l < layers; ++l) {
+            c.state[l] = pools->state[l];
+            c.rec[l] = pools->rec[l];
+        }
+        c.rec_slot = rec_slot;
+        c.rec_stride = gdn_rec_stride(pools->rec_tokens);
+        c.hv = pools->num_v_heads;
+        c.num_slots = pools->num_state_slots;
+        c.num_rec_slots = pools->num_rec_slots;
+        c.T = pools->rec_tokens;
+    }
+    if (conv) {
+        ConvParams& v = c.conv;
+        for (int32_t l = 0; l < layers; ++l) {
+            v.state[l] = conv->state[l];
+            v.x[l] = conv->x[l];
+        }
+        v.tok_start = conv_tok_start;
+        v.row_bytes = conv_row_bytes(conv);
+        v.x_tok_bytes = conv->x_tok_stride * conv_elem_bytes(conv);
+        v.num_tokens = conv->num_tokens;
+        v.state_len = conv->state_len;
+        v.num_slots = conv->num_slots;
+        v.pieces = (int32_t)(v.row_bytes / 16);
+        v.wgs_per_row = (int32_t)conv_per_row;
+        c.conv_wgs = (int64_t)num_rows * layers * conv_per_row;
+    }
+    const bool bf16 = pools && pools->state_dtype == GDN_STATE_BF16;
+    return launched(launch_commit(c, bf16, bnd_len != nullptr, (hipStream_t)stream));
+}
+
 int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
                               const int32_t* src_slot, const int32_t* dst_slot,
                               const int32_t* rec_slot, const int32_t* n_accept,
                               const int32_t* bnd_len, const int32_t* bnd_slot,
                               int32_t* err_flags, void* stream)
 {
-    int32_t st = check_pools(pools);
-    if (st) return st;
-    if (num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads * pools->num_layers * 8 > INT32_MAX)
-        return GDN_ERR_SHAPE;
-    for (int32_t l = 0; l < pools->num_layers; ++l)
-        if ((st = check_layer_ptrs(pools, l, true))) return st;
-    if (!src_slot || !dst_slot || !rec_slot || !n_accept) return GDN_ERR_NULL;
-    if ((bnd_len == nullptr) != (bnd_slot == nullptr)) return GDN_ERR_NULL;
-    if (num_rows == 0) return GDN_OK;
-
-    CommitParams c;
-    memset(&c, 0, sizeof(c));
-    for (int32_t l = 0; l < pools->num_layers; ++l) {
-        c.state[l] = pools->state[l];
-        c.rec[l] = pools->rec[l];
-    }
-    c.src = src_slot;
-    c.dst = dst_slot;
-    c.rec_slot = rec_slot;
-    c.n = n_accept;
-    c.bnd_len = bnd_len;
-    c.bnd_slot = bnd_slot;
-    c.err = err_flags;
-    c.rec_stride = gdn_rec_stride(pools->rec_tokens);
-    c.num_layers = pools->num_layers;
-    c.num_rows = num_rows;
-    c.hv = pools->num_v_heads;
-    c.num_slots = pools->num_state_slots;
-    c.num_rec_slots = pools->num_rec_slots;
-    c.T = pools->rec_tokens;
-    return launched(launch_commit(c, pools->state_dtype == GDN_STATE_BF16, bnd_len != nullptr,
-                                  (hipStream_t)stream));
+    if (!pools) return GDN_ERR_NULL;
+    return gdn_commit_all_layers_conv(pools, nullptr, num_rows, src_slot, dst_slot, rec_slot,
+                                      n_accept, bnd_len, bnd_slot, nullptr, err_flags, stream);
 }
 
 int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers, int32_t num_rows,

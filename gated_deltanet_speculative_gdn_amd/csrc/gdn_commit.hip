@@ -92,9 +92,92 @@ template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
     __device__ static int col0(int t) { return 8 * (t & 15); }
 };
 
-template <typename StateT, bool ALIGN, int SPLIT, bool NT>
+// Row check shared by the state replay and the conv compaction of one launch:
+// a row with bad data is skipped by both parts.
+template <bool ALIGN>
+__device__ int commit_row_error(const CommitParams& p, int b, int n, int src, int dst, int bl, int bs)
+{
+    int err = 0;
+    if (n < 0 || dst < 0) err |= kRowN;
+    if (ALIGN && bl != 0 && (bl < 0 || bl >= n || bs < 0)) err |= kRowBnd;
+    if (p.ssm_wgs > 0) {
+        const int rs = p.rec_slot[b];
+        if (n > p.T) err |= kRowN;
+        if (src >= p.num_slots || dst >= p.num_slots) err |= kRowSlot;
+        if (ALIGN && bl > 0 && bs >= p.num_slots) err |= kRowBnd;
+        if (rs < 0 || rs >= p.num_rec_slots) err |= kRowRec;
+    }
+    if (p.conv_wgs > 0) {
+        const int ts = p.conv.tok_start[b];
+        if (src >= p.conv.num_slots || dst >= p.conv.num_slots) err |= kRowSlot;
+        if (ALIGN && bl > 0 && bs >= p.conv.num_slots) err |= kRowBnd;
+        if (ts < 0 || (int64_t)ts + n > p.conv.num_tokens) err |= kRowWin;
+    }
+    return err;
+}
+
+// Short-conv state compaction of one (layer, row, chunk of 256 16-byte column
+// pieces): row i of the final state is row n + i of [source rows 0..Ls-1,
+// inputs x_0..x_{n-1}], row i of the boundary state row bnd_len + i. Each
+// thread copies one column piece down the rows, final rows first, then the
+// boundary rows; it reads row n + i (or bnd_len + i > i) before it writes row
+// i, so a destination equal to the source is shifted in place correctly. No
+// arithmetic: the bytes are moved as they are.
+template <bool ALIGN>
+__device__ void conv_compact(const CommitParams& p, int64_t id)
+{
+    static_assert(kConvPiecesPerWg == kThreads, "one piece per thread");
+    const ConvParams& c = p.conv;
+    const int chunk = (int)(id % c.wgs_per_row);
+    const int64_t lb = id / c.wgs_per_row;
+    const int b = (int)(lb % p.num_rows);
+    const int layer = (int)(lb / p.num_rows);
+    const int n = p.n[b];
+    if (n == 0) return;
+    const int src = p.src[b];
+    if (src < 0) return;
+    const int dst = p.dst[b];
+    const int ts = c.tok_start[b];
+    int bl = 0, bs = -1;
+    if constexpr (ALIGN) {
+        bl = p.bnd_len[b];
+        bs = p.bnd_slot[b];
+    }
+    const int err = commit_row_error<ALIGN>(p, b, n, src, dst, bl, bs);
+    if (err) {
+        if (threadIdx.x == 0 && chunk == 0 && layer == 0 && p.err) atomicOr(p.err, err);
+        return;
+    }
+    const int piece = chunk * kThreads + (int)threadIdx.x;
+    if (piece >= c.pieces) return;
+    const int Ls = c.state_len;
+    const int64_t slot_bytes = (int64_t)Ls * c.row_bytes;
+    char* pool = static_cast<char*>(c.state[layer]) + 16 * (int64_t)piece;
+    const char* srcp = pool + src * slot_bytes;
+    const char* xp = static_cast<const char*>(c.x[layer]) + (int64_t)ts * c.x_tok_bytes + 16 * (int64_t)piece;
+    auto row = [&](int r) -> u32x4 {
+        const char* q = r < Ls ? srcp + r * c.row_bytes : xp + (int64_t)(r - Ls) * c.x_tok_bytes;
+        return *reinterpret_cast<const u32x4*>(q);
+    };
+    char* dstp = pool + dst * slot_bytes;
+    for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(dstp + i * c.row_bytes) = row(n + i);
+    if constexpr (ALIGN) {
+        if (bl > 0 && bs != dst) {
+            char* bp = pool + bs * slot_bytes;
+            for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(bp + i * c.row_bytes) = row(bl + i);
+        }
+    }
+}
+
+template <typename StateT, bool ALIGN, int SPLIT, bool NT, bool CONV>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
+    if constexpr (CONV) {
+        if ((int64_t)blockIdx.x >= p.ssm_wgs) {
+            conv_compact<ALIGN>(p, (int64_t)blockIdx.x - p.ssm_wgs);
+            return;
+        }
+    }
     typedef HeadIO<StateT, SPLIT> IO;
     constexpr int kRows = kDim / SPLIT;   // rows of the head this workgroup owns
     extern __shared__ float lds[];
@@ -104,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     float* g_l = lds + 2 * T * kDim;  // [n] decays
 
     // logical id: (layer, row, value head, part), XCD-contiguous
-    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, p.ssm_wgs) : blockIdx.x;
     const int part = (int)(wg % SPLIT);
     const int64_t head_id = wg / SPLIT;
     const int hv = (int)(head_id % p.hv);
@@ -124,11 +207,7 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         bl = p.bnd_len[b];
         bs = p.bnd_slot[b];
     }
-    int err = 0;
-    if (n < 0 || n > T || dst < 0) err |= kRowN;
-    if (src >= p.num_slots || dst >= p.num_slots) err |= kRowSlot;
-    if (rs < 0 || rs >= p.num_rec_slots) err |= kRowRec;
-    if (ALIGN && bl != 0 && (bl < 0 || bl >= n || bs < 0 || bs >= p.num_slots)) err |= kRowBnd;
+    const int err = commit_row_error<ALIGN>(p, b, n, src, dst, bl, bs);
     if (err) {
         if (threadIdx.x == 0 && hv == 0 && layer == 0 && part == 0 && p.err) atomicOr(p.err, err);
         return;
@@ -232,9 +311,12 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
 {
     CommitParams args = p;
     void* kargs[] = {&args};
-    const uint64_t grid = (uint64_t)p.num_layers * p.num_rows * p.hv * SPLIT;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT>),
-                           dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
+    args.ssm_wgs = p.hv > 0 ? (int64_t)p.num_layers * p.num_rows * p.hv * SPLIT : 0;
+    const uint64_t grid = (uint64_t)(args.ssm_wgs + p.conv_wgs);
+    const void* fn = p.conv_wgs > 0
+        ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true>)
+        : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
 }
 
 template <bool ALIGN, int SPLIT, bool NT>

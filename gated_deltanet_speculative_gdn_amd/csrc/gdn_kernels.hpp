@@ -35,6 +35,21 @@ struct VerifyParams {
     bool out_bf16;            // outputs rounded to bf16 (nearest even)
 };
 
+// Short-conv state compaction, run by extra workgroups of the commit launch:
+// one 16-byte column piece per thread, one workgroup per this many pieces.
+constexpr int kConvPiecesPerWg = 256;
+struct ConvParams {
+    void* state[GDN_MAX_LAYERS];        // [slots][state_len][row_bytes]
+    const void* x[GDN_MAX_LAYERS];      // [tokens][x_tok_bytes]
+    const int32_t* tok_start;
+    int64_t row_bytes;                  // bytes per state row, a multiple of 16
+    int64_t x_tok_bytes;                // bytes between tokens of x, a multiple of 16
+    int64_t num_tokens;
+    int32_t state_len, num_slots;
+    int32_t pieces;                     // 16-byte pieces per row
+    int32_t wgs_per_row;                // workgroups per (layer, row)
+};
+
 // The all-layer commit.
 struct CommitParams {
     void* state[GDN_MAX_LAYERS];
@@ -48,6 +63,9 @@ struct CommitParams {
     int32_t* err;
     int64_t rec_stride;
     int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
+    int64_t ssm_wgs;          // workgroups of the state replay (the first ones of the grid)
+    int64_t conv_wgs;         // workgroups of the conv compaction (after them; 0 = none)
+    ConvParams conv;
 };
 
 // The native baseline's accepted-state copy.

@@ -246,6 +246,36 @@ def make_raw_gates(wl: Workload, device="cpu", seed: int | None = None) -> RawGa
     return RawGates(*(torch.as_tensor(x, device=dev) for x in (a, b, A_log, dt_bias)))
 
 
+@dataclass
+class ConvInputs:
+    """Short-conv state pools of every layer and the step's conv inputs."""
+    state: torch.Tensor    # [L][slots][state_len][C]
+    x: torch.Tensor        # [L][tokens][C]
+
+
+CONV_SEED_OFFSET = 104729
+
+
+def make_conv(wl: Workload, state_len: int = 3, dtype=torch.bfloat16, device="cpu",
+              seed: int | None = None, channels: int | None = None) -> ConvInputs:
+    """Draw short-conv states and inputs for a workload from a stream of their
+    own: C = (2 HK + HV) * 128 channels by default (the mixed q/k/v a GDN
+    layer's short conv runs over), values N(0, 1); state_len = (kernel width
+    - 1) * dilation, 3 for a width-4 conv."""
+    s = wl.spec
+    seed = (s.seed if seed is None else seed) + CONV_SEED_OFFSET
+    C = (2 * s.hk + s.hv) * 128 if channels is None else channels
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    state = torch.empty((s.layers, s.num_slots, state_len, C), dtype=dtype, device=dev)
+    x = torch.empty((s.layers, wl.tokens, C), dtype=dtype, device=dev)
+    for layer in range(s.layers):
+        state[layer] = _normal((s.num_slots, state_len, C), gen, dev).to(dtype)
+        x[layer] = _normal((wl.tokens, C), gen, dev).to(dtype)
+    return ConvInputs(state, x)
+
+
 def acceptance_rate_counts(rng: np.random.Generator, rows: int,
                            rates=(0.856, 0.694, 0.558, 0.457, 0.376)) -> np.ndarray:
     """Accepted counts drawn from per-position acceptance rates (a draft token

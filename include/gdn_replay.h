@@ -198,6 +198,67 @@ int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
                               int32_t* err_flags, void* stream);
 
 /*
+ * Short-conv state pools for the all-layer commit ([vLLM] Purpose: the short
+ * conv beside each GDN layer compacts its accepted window with the same plan;
+ * Test Plan: spec conv + commit against the stock token-by-token decode).
+ *
+ * A causal short conv of kernel width W and dilation d keeps the last
+ * L_s = (W - 1) * d inputs of every channel. Its state of one slot is
+ * [L_s][C] (oldest row first, channels contiguous); decoding one token with
+ * input x drops the oldest row and appends x. After a verify window the
+ * commit keeps, for n accepted tokens, the last L_s rows of
+ * [state rows 0..L_s-1, x_0 .. x_{n-1}].
+ *
+ * state[l]: device, layer l's conv pool, [num_slots][state_len][channels].
+ * x[l]: device, layer l's conv inputs of this step, [num_tokens][x_tok_stride]
+ *   (channels contiguous, same dtype as the state); row b's window starts at
+ *   token tok_start[b] (the commit's conv_tok_start argument).
+ * Bytes per state row (channels * element size) and per x token stride must be
+ * multiples of 16; pointers 16-byte aligned.
+ */
+typedef struct gdn_conv_pools {
+    int32_t num_layers;       /* 1..GDN_MAX_LAYERS */
+    int32_t channels;         /* C >= 1 */
+    int32_t state_len;        /* L_s, 1..GDN_MAX_CONV_STATE */
+    int32_t dtype;            /* gdn_state_dtype of states and inputs */
+    int32_t num_slots;        /* >= 1 */
+    int32_t reserved;         /* set to 0 */
+    int64_t x_tok_stride;     /* elements between consecutive tokens of x */
+    int64_t num_tokens;       /* tokens addressable in x */
+    void* state[GDN_MAX_LAYERS];
+    const void* x[GDN_MAX_LAYERS];
+} gdn_conv_pools;
+
+#define GDN_MAX_CONV_STATE 1024
+
+/*
+ * gdn_commit_all_layers_conv -- gdn_commit_all_layers plus the short-conv
+ * state compaction of the same rows, in the same single launch ([vLLM]
+ * Purpose; review thread: plan, conv and state launches per group cost host
+ * time, one launch over everything is preferred).
+ *
+ * pools may be NULL (conv states only; rec_slot is then unused) and conv may
+ * be NULL (identical to gdn_commit_all_layers). With both, num_layers must
+ * match. The SSM part is exactly gdn_commit_all_layers. For the conv part,
+ * row b with n = n_accept[b] > 0 and src_slot[b] >= 0 writes
+ *   final:    rows i = 0..L_s-1 of dst_slot[b] = row n + i of
+ *             [src rows 0..L_s-1, x[tok_start[b]] .. x[tok_start[b] + n - 1]]
+ *   boundary: when 0 < bnd_len[b] < n and bnd_slot[b] != dst_slot[b], rows
+ *             i of bnd_slot[b] = row bnd_len[b] + i of the same sequence,
+ * final first, then boundary, each from values read before it is written over
+ * (a final or boundary slot equal to the source slot is safe).
+ * conv_tok_start: device int32 [num_rows], needed when conv is given.
+ * Errors: as gdn_commit_all_layers; GDN_ROW_SLOT for conv slots outside
+ * [0, conv->num_slots), GDN_ROW_WIN for a window outside x.
+ */
+int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools* conv,
+                                   int32_t num_rows, const int32_t* src_slot,
+                                   const int32_t* dst_slot, const int32_t* rec_slot,
+                                   const int32_t* n_accept, const int32_t* bnd_len,
+                                   const int32_t* bnd_slot, const int32_t* conv_tok_start,
+                                   int32_t* err_flags, void* stream);
+
+/*
  * gdn_align_plan -- align-mode slots of each row from its block table
  * ([vLLM] Purpose; Commits items 3 and 6).
  *

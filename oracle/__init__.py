@@ -15,6 +15,10 @@ shared library and marshals numpy arrays:
   token positions.
 * :func:`bf16_to_f32`, :func:`f32_to_bf16_rne` -- exact widening and
   round-to-nearest-even narrowing.
+* :func:`raw_gates` -- log-gate and write strength from raw gate inputs.
+* :func:`conv_decode`, :func:`conv_commit` -- the short-conv state, one token
+  at a time (numpy; the state is a window of inputs, so this is data movement
+  only).
 
 Sources: vLLM PR "[Spec Decode][Qwen4Exp] RecoverSSM for Qwen GDN and the PLE
 short conv" (Purpose; Commits items 3 and 6; Test Plan; Test Result) and the
@@ -189,6 +193,28 @@ def raw_gates(a, b, A_log, dt_bias, *, dtype=np.float32):
           lg.reshape(-1), be.reshape(-1)) != 0:
         raise ValueError("raw_gates: bad argument")
     return lg, be
+
+
+def conv_decode(state, x) -> np.ndarray:
+    """The stock token-by-token decode of a causal short conv's state
+    (vLLM RecoverSSM PR, Purpose and Test Plan: the short conv's accepted
+    window is compacted, checked against token-by-token decode). The state
+    [L_s][C] holds the last L_s inputs, oldest first; decoding input row x_t
+    drops the oldest row and appends x_t. x [n][C]. Returns the states after
+    0, 1, .., n tokens: [n + 1][L_s][C]."""
+    s = np.array(state, copy=True)
+    out = [s.copy()]
+    for t in range(len(x)):
+        s = np.concatenate([s[1:], np.asarray(x)[t:t + 1]], axis=0)
+        out.append(s.copy())
+    return np.stack(out)
+
+
+def conv_commit(state, x, n, bnd_len=0):
+    """Final conv state after n accepted inputs x[:n], and the state after
+    bnd_len inputs when 0 < bnd_len < n (else None)."""
+    walk = conv_decode(state, np.asarray(x)[:n])
+    return walk[n], (walk[bnd_len] if 0 < bnd_len < n else None)
 
 
 def bf16_to_f32(bits) -> np.ndarray:

@@ -188,3 +188,44 @@ def test_native_rejects_malformed(lib):
     assert lib.gdn_native_accept(C.byref(p), snaps, 4, ROWS, ROWS, None, None) == E_NULL
     snaps = (C.c_void_p * 2)(0xB0000, 0xC0000)
     assert lib.gdn_native_accept(C.byref(p), snaps, 0, ROWS, ROWS, None, None) == OK
+
+
+def good_conv(layers=2):
+    c = B.gdn_conv_pools()
+    c.num_layers, c.channels, c.state_len, c.dtype, c.num_slots = layers, 8192, 3, 1, 8
+    c.x_tok_stride, c.num_tokens = 8192, 64
+    for i in range(layers):
+        c.state[i] = 0xA0000 + i * 0x100000     # never dereferenced: calls below are rejected
+        c.x[i] = 0xB0000 + i * 0x100000
+    return c
+
+
+def commit_conv(lib, pools, conv, rows=4, tok=ROWS, rec=ROWS):
+    return lib.gdn_commit_all_layers_conv(C.byref(pools) if pools is not None else None,
+                                          C.byref(conv) if conv is not None else None, rows,
+                                          ROWS, ROWS, rec, ROWS, None, None, tok, None, None)
+
+
+def test_commit_conv_validation(lib):
+    assert commit_conv(lib, good_pools(), good_conv(), rows=0) == OK
+    assert commit_conv(lib, None, good_conv(), rows=0, rec=None) == OK   # conv states only
+    assert commit_conv(lib, good_pools(), None, rows=0) == OK             # plain commit
+    assert commit_conv(lib, None, None) == E_NULL
+    assert commit_conv(lib, good_pools(), good_conv(), tok=None) == E_NULL
+    assert commit_conv(lib, good_pools(), good_conv(layers=3)) == E_SHAPE
+    c = good_conv(); c.dtype = 2
+    assert commit_conv(lib, None, c) == E_DTYPE
+    c = good_conv(); c.state_len = 0
+    assert commit_conv(lib, None, c) == E_SHAPE
+    c = good_conv(); c.state_len = 1025
+    assert commit_conv(lib, None, c) == E_SHAPE
+    c = good_conv(); c.channels = 12; c.x_tok_stride = 16          # 24-byte bf16 rows
+    assert commit_conv(lib, None, c) == E_ALIGN
+    c = good_conv(); c.x_tok_stride = 8196                            # 16392-byte token stride
+    assert commit_conv(lib, None, c) == E_ALIGN
+    c = good_conv(); c.x_tok_stride = 4096                            # shorter than a row
+    assert commit_conv(lib, None, c) == E_SHAPE
+    c = good_conv(); c.x[1] = None
+    assert commit_conv(lib, None, c) == E_NULL
+    c = good_conv(); c.state[0] = 0xA0008
+    assert commit_conv(lib, None, c) == E_ALIGN

@@ -1,0 +1,139 @@
+"""GPU parity of the short-conv state compaction that runs in the same launch
+as the all-layer commit (vLLM RecoverSSM PR, Purpose: the short conv compacts
+its accepted window with the same plan; Test Plan: spec conv + commit against
+the stock token-by-token decode, bit-identical states).
+
+The compaction moves values without arithmetic, so the bar is bit-exact: every
+conv state written equals the oracle's token-by-token decode, every other slot
+keeps its bits, and the state-replay part of the fused launch equals a plain
+gdn_commit_all_layers on a copy of the pools bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_deltanet_speculative_gdn_amd as G
+from gated_deltanet_speculative_gdn_amd import workloads as W
+from gpu_harness import Harness, dev_i32
+from test_parity_gpu import pool_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def raw(t: torch.Tensor) -> np.ndarray:
+    """Bits of a device tensor as a numpy array (exact for fp32 and bf16)."""
+    t = t.detach().contiguous()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).cpu().numpy()
+
+
+def expected_pool(pre_layer, x_layer, rows, src, dst, n, ts, bnd_len=None, bnd_slot=None):
+    """Conv pool of one layer after the commit, from the oracle's token walk:
+    final states first, then boundary states, each from the pre-commit source."""
+    out = pre_layer.copy()
+    finals, bnds = [], []
+    for b in rows:
+        if n[b] == 0 or src[b] < 0:
+            continue
+        bl = 0 if bnd_len is None else int(bnd_len[b])
+        fin, bnd = oracle.conv_commit(pre_layer[src[b]], x_layer[ts[b]: ts[b] + n[b]], int(n[b]), bl)
+        finals.append((dst[b], fin))
+        if bnd is not None and bnd_slot[b] != dst[b]:
+            bnds.append((bnd_slot[b], bnd))
+    for slot, v in finals:
+        out[slot] = v
+    for slot, v in bnds:
+        out[slot] = v
+    return out
+
+
+@pytest.mark.parametrize("conv_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_fused_commit_mtp(gdn, conv_dtype):
+    """Three layers of the 16-row workload: verify, then one launch commits the
+    recurrent states and compacts the conv states in place (dst = src)."""
+    spec = W.shrink(W.ALL_LAYER, layers=3)
+    wl = W.make_workload(spec, device="cuda")
+    cv = W.make_conv(wl, state_len=3, dtype=conv_dtype, device="cuda")
+    h = Harness(wl)
+    h.verify_all()
+    torch.cuda.synchronize()
+    ref_state = wl.state.clone()
+    ref_pools = G.Pools(ref_state, h.rec, spec.hk, spec.rec_tokens)
+    G.gdn_commit_all_layers(ref_pools, h.state_slot, h.state_slot, h.rec_slot, h.n_accept,
+                            err_flags=h.err)
+    pre = raw(cv.state)
+    x = raw(cv.x)
+    conv = G.ConvPools(cv.state, cv.x)
+    G.gdn_commit_all_layers_conv(h.pools, conv, h.state_slot, h.state_slot, h.rec_slot,
+                                 h.n_accept, conv_tok_start=h.tok_start, err_flags=h.err)
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    assert torch.equal(pool_bits(wl.state), pool_bits(ref_state)), "state replay differs"
+    got = raw(cv.state)
+    rows = range(spec.rows)
+    for layer in range(spec.layers):
+        exp = expected_pool(pre[layer], x[layer], rows, wl.state_slot, wl.state_slot,
+                            wl.n_accept, wl.tok_start)
+        np.testing.assert_array_equal(got[layer], exp, err_msg=f"layer {layer}")
+
+
+def test_conv_only_align_plan_dilated(gdn):
+    """Conv states only (no recurrent pools), a dilated conv (L_s = 12), fp32,
+    260 channels (a partial workgroup), align-mode slots from the oracle's
+    plan: windows that start on a block boundary, end on one, and cross one
+    (boundary written into the source slot, read before it is overwritten)."""
+    rng = np.random.default_rng(71)
+    rows, blk, max_n, Ls, C, slots = 24, 8, 4, 12, 260, 256
+    r = np.tile(np.arange(blk), rows // blk)
+    p0 = (8 * rng.integers(3, 9, rows) + r).astype(np.int32)
+    p0[p0 < 1] = 1
+    n = rng.integers(0, max_n + 1, rows).astype(np.int32)
+    n[r >= 5] = 4                                   # these windows cross a boundary
+    cols = int(((p0 + max_n - 1) // blk).max()) + 1
+    perm = rng.permutation(slots)[: rows * cols].reshape(rows, cols).astype(np.int32)
+    src, dst, bl, bs, perr = oracle.align_plan(p0, n, perm, blk, max_n)
+    assert (perr == 0).all() and (bl > 0).any() and ((bs == src) & (bl > 0)).any()
+    L = 2
+    state = torch.randn((L, slots, Ls, C), device="cuda")
+    x = torch.randn((L, rows * max_n, C), device="cuda")
+    ts = (np.arange(rows) * max_n).astype(np.int32)
+    pre = raw(state)
+    xs = raw(x)
+    conv = G.ConvPools(state, x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gdn_commit_all_layers_conv(None, conv, dev_i32(src), dev_i32(dst), None, dev_i32(n),
+                                 dev_i32(bl), dev_i32(bs), dev_i32(ts), err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = raw(state)
+    for layer in range(L):
+        exp = expected_pool(pre[layer], xs[layer], range(rows), src, dst, n, ts, bl, bs)
+        np.testing.assert_array_equal(got[layer], exp, err_msg=f"layer {layer}")
+
+
+def test_fused_row_error_skips_both_parts(gdn):
+    """A row whose conv window runs past the inputs is skipped by the state
+    replay and by the conv compaction alike (GDN_ROW_WIN); the other rows are
+    committed as usual."""
+    spec = W.shrink(W.ALL_LAYER, layers=1, rows=4)
+    wl = W.make_workload(spec, device="cuda", seed=72)
+    wl.n_accept = np.array([3, 2, 4, 1], np.int32)
+    cv = W.make_conv(wl, state_len=3, device="cuda")
+    h = Harness(wl)
+    h.verify_all()
+    torch.cuda.synchronize()
+    pre_state = wl.state.clone()
+    pre_conv = cv.state.clone()
+    ts = wl.tok_start.copy()
+    ts[2] = wl.tokens - 1                            # window of 4 tokens past the end of x
+    conv = G.ConvPools(cv.state, cv.x)
+    G.gdn_commit_all_layers_conv(h.pools, conv, h.state_slot, h.state_slot, h.rec_slot,
+                                 h.n_accept, conv_tok_start=dev_i32(ts), err_flags=h.err)
+    torch.cuda.synchronize()
+    assert h.err_value() == G.ROW_WIN
+    bad = int(wl.state_slot[2])
+    assert torch.equal(pool_bits(wl.state[0, bad]), pool_bits(pre_state[0, bad]))
+    assert torch.equal(pool_bits(cv.state[0, bad]), pool_bits(pre_conv[0, bad]))
+    for b in (0, 1, 3):
+        s = int(wl.state_slot[b])
+        assert not torch.equal(pool_bits(cv.state[0, s]), pool_bits(pre_conv[0, s]))

@@ -418,3 +418,38 @@ def test_raw_gates_fp32_close_to_fp64():
     lg64, be64 = oracle.raw_gates(a, b, A_log, dtb, dtype=np.float64)
     np.testing.assert_allclose(lg32, lg64, rtol=4e-7)
     np.testing.assert_allclose(be32, be64, rtol=4e-7)
+
+
+# ---- short-conv state (token-by-token decode) ---------------------------------
+
+def test_conv_decode_hand_worked():
+    """L_s = 3 rows of 2 channels, two inputs, worked by hand: each token drops
+    the oldest row and appends its input."""
+    state = np.array([[1, 2], [3, 4], [5, 6]], np.float32)
+    x = np.array([[7, 8], [9, 10]], np.float32)
+    walk = oracle.conv_decode(state, x)
+    np.testing.assert_array_equal(walk[0], state)
+    np.testing.assert_array_equal(walk[1], [[3, 4], [5, 6], [7, 8]])
+    np.testing.assert_array_equal(walk[2], [[5, 6], [7, 8], [9, 10]])
+    fin, bnd = oracle.conv_commit(state, x, 2, bnd_len=1)
+    np.testing.assert_array_equal(fin, walk[2])
+    np.testing.assert_array_equal(bnd, walk[1])
+    assert oracle.conv_commit(state, x, 2, bnd_len=2)[1] is None   # boundary at n: none
+
+
+@pytest.mark.parametrize("Ls", [1, 3, 12])
+def test_conv_decode_is_a_sliding_window(Ls):
+    """After n tokens the state is rows n .. n+Ls-1 of [state; x] (closed
+    form of the window), for n below and above L_s; n = 0 keeps the state;
+    decoding in two pieces equals decoding at once."""
+    rng = np.random.default_rng(Ls)
+    state = rng.normal(size=(Ls, 8)).astype(np.float32)
+    x = rng.normal(size=(Ls + 6, 8)).astype(np.float32)
+    seq = np.concatenate([state, x])
+    walk = oracle.conv_decode(state, x)
+    for n in range(len(x) + 1):
+        np.testing.assert_array_equal(walk[n], seq[n:n + Ls])
+    np.testing.assert_array_equal(oracle.conv_commit(state, x, 0)[0], state)
+    a = 4
+    mid = oracle.conv_decode(state, x[:a])[a]
+    np.testing.assert_array_equal(oracle.conv_decode(mid, x[a:])[-1], walk[-1])
