@@ -1,0 +1,70 @@
+"""GPU parity at the interface's limits: the longest windows (T = 16 records,
+every position in one window), a window placed after pending records (record
+positions 5..15 verified after positions 0..4), windows of 8, and a commit
+over the most layers a pool set may hold (64). Bars as in test_parity_gpu."""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_speculative_gdn_amd as G
+from gated_deltanet_speculative_gdn_amd import workloads as W
+from gpu_harness import Harness, dev_i32
+from test_parity_gpu import check_layer, pool_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T", [8, 16])
+def test_longest_windows(gdn, T):
+    spec = W.shrink(W.SINGLE_LAYER, rows=8, window=T, rec_tokens=T, n_lo=1, n_hi=T)
+    wl = W.make_workload(spec, device="cuda", seed=80 + T)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre))
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    check_layer(h, 0, np.arange(spec.rows), wl.n_accept, pre[0])
+
+
+def test_window_after_pending_records(gdn):
+    """Positions 0..4 verified first, then positions 5..15 with the first five
+    records pending (ring base 5, window 11, T = 16): together the outputs and
+    records of one 16-token window, checked against the native rule over all
+    16 tokens, then a commit of n = 1..16."""
+    T = 16
+    spec = W.shrink(W.SINGLE_LAYER, rows=8, window=T, rec_tokens=T, n_lo=1, n_hi=T)
+    wl = W.make_workload(spec, device="cuda", seed=90)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    rows = spec.rows
+    first = dev_i32(np.full(rows, 5))
+    second = dev_i32(np.full(rows, T - 5))
+    base0 = dev_i32(np.zeros(rows))
+    base5 = dev_i32(np.full(rows, 5))
+    ts0 = dev_i32(wl.tok_start)
+    ts5 = dev_i32(wl.tok_start + 5)
+    for ts, w, base in ((ts0, first, base0), (ts5, second, base5)):
+        G.gdn_verify(h.pools, 0, h.state_slot, h.rec_slot, ts, w, base, wl.q(0), wl.k(0),
+                     wl.v(0), wl.a[0], wl.beta[0], h.out[0], err_flags=h.err)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre))
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    check_layer(h, 0, np.arange(rows), wl.n_accept, pre[0])
+
+
+def test_commit_over_64_layers(gdn):
+    spec = W.shrink(W.ALL_LAYER, layers=G.GDN_MAX_LAYERS, rows=3, hv=2, hk=1, num_slots=8)
+    wl = W.make_workload(spec, device="cuda", seed=91)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    for layer in range(spec.layers):
+        check_layer(h, layer, np.arange(spec.rows), wl.n_accept, pre[layer])
