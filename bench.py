@@ -34,6 +34,7 @@ from gated_deltanet_speculative_gdn_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 REC_TOKEN_BYTES = (128 + 128 + 1) * 4           # correction, key, gate (fp32)
+PAYLOAD_TOKEN_BYTES = (128 + 128) * 2 + 2 * 4    # raw key, raw value (bf16), gate, beta (fp32)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "commit_counters.json")
 KERNEL_SOURCES = ["gated_deltanet_speculative_gdn_amd/csrc/gdn_commit.hip",
                   "gated_deltanet_speculative_gdn_amd/csrc/gdn_device.hpp",
@@ -59,11 +60,13 @@ def i32(x):
 class Step:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, wl, raw_gates=False, out_dtype=torch.float32, conv=None):
+    def __init__(self, wl, raw_gates=False, out_dtype=torch.float32, conv=None,
+                 record_kind=G.RECORD_CORRECTION):
         s = wl.spec
         self.wl, self.s = wl, s
-        self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens)
-        self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens)
+        self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens,
+                                         record_kind=record_kind)
+        self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens, record_kind)
         self.out = torch.zeros((s.layers, wl.tokens, s.hv, s.dv), dtype=out_dtype, device="cuda")
         self.rg = W.make_raw_gates(wl, device="cuda") if raw_gates else None
         self.conv = G.ConvPools(conv.state, conv.x) if conv is not None else None
@@ -116,7 +119,7 @@ class Step:
         G.gdn_native_accept(self.pools, self.snaps, self.slot, self.n, err_flags=self.err)
 
 
-def accounting(wl, out_bytes=4, raw_gates=False, conv=None):
+def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_BYTES):
     """Update counts and algorithmic HBM bytes of one step (out_bytes: bytes
     per output element; raw gates add the per-head parameters; conv: the
     short-conv states compacted in the commit launch)."""
@@ -127,15 +130,15 @@ def accounting(wl, out_bytes=4, raw_gates=False, conv=None):
     n = wl.n_accept[real].astype(np.int64)
     verify_updates = int(s.layers * s.hv * w.sum())
     commit_updates = int(s.layers * s.hv * n.sum())
-    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + REC_TOKEN_BYTES)
+    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + rec_bytes)
     verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok + (s.hv * 8 if raw_gates else 0))
-    commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * REC_TOKEN_BYTES))
+    commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * rec_bytes))
     if conv is not None:
         Ls, C = conv.state.shape[2], conv.state.shape[3]
         row = C * conv.state.element_size()
         # per live row and layer: read L_s state rows and n inputs, write L_s rows
         commit_bytes += int(s.layers * ((n > 0).sum() * 2 * Ls * row + n.sum() * row))
-    native_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * (per_tok - s.hv * REC_TOKEN_BYTES)
+    native_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * (per_tok - s.hv * rec_bytes)
                              + w.sum() * s.hv * sb)
     accept_bytes = int(s.layers * s.hv * (n > 0).sum() * 2 * sb)
     return dict(verify_updates=verify_updates, commit_updates=commit_updates,
@@ -230,6 +233,9 @@ def main():
                     help="log: log-gate and beta given; raw: gates formed in the kernel from "
                          "raw a, b with per-head A_log, dt_bias")
     ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--record", default="correction", choices=["correction", "payload"],
+                    help="correction: (delta, k_hat, gate) records, elementwise commit; payload: "
+                         "(k, v, gate, beta) records, the commit recomputes the corrections")
     ap.add_argument("--conv", action="store_true",
                     help="also compact bf16 short-conv states (width-4 conv over the mixed "
                          "q/k/v channels) in the commit launch")
@@ -252,10 +258,13 @@ def main():
     log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
     wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
     conv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if args.conv else None
+    payload = args.record == "payload"
     acc = accounting(wl, out_bytes=2 if args.out_dtype == "bf16" else 4,
-                     raw_gates=args.gating == "raw", conv=conv)
+                     raw_gates=args.gating == "raw", conv=conv,
+                     rec_bytes=PAYLOAD_TOKEN_BYTES if payload else REC_TOKEN_BYTES)
     st = Step(wl, raw_gates=args.gating == "raw",
-              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32, conv=conv)
+              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32, conv=conv,
+              record_kind=G.RECORD_PAYLOAD if payload else G.RECORD_CORRECTION)
     L = spec.layers
 
     # warm-up (also loads the code object before capture)
@@ -297,6 +306,7 @@ def main():
                    "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
                    "gating": args.gating, "out_dtype": args.out_dtype, "conv_states": args.conv,
+                   "record": args.record,
                    "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
         "roofline": {"bound": "hbm", "kernel": "commit_all_layers",
                      "achieved": com_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -6,7 +6,8 @@ marshalling only), the in-tree build script and the seeded workload
 generators.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, GDN_MAX_LAYERS, GDN_MAX_REC_TOKENS, ConvPools, GdnError, Pools, ROW_BND, ROW_N,
+    EXPORTS, GDN_MAX_LAYERS, GDN_MAX_REC_TOKENS, RECORD_CORRECTION, RECORD_PAYLOAD, ConvPools,
+    GdnError, Pools, ROW_BND, ROW_N,
     ROW_POS, ROW_REC, ROW_SLOT, ROW_TABLE, ROW_WIN, gdn_align_plan, gdn_commit_all_layers,
     gdn_commit_all_layers_conv, gdn_native_accept, gdn_native_window, gdn_verify, load_library,
     rec_stride,

@@ -19,12 +19,13 @@ GDN_HEAD_DIM = 128
 GDN_MAX_REC_TOKENS = 16
 GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
 GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
+RECORD_CORRECTION, RECORD_PAYLOAD = 0, 1   # gdn_record_kind
 OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv", "gdn_align_plan",
-           "gdn_native_window", "gdn_native_accept", "gdn_rec_stride", "gdn_status_string",
-           "gdn_abi_version")
+           "gdn_native_window", "gdn_native_accept", "gdn_rec_stride", "gdn_record_stride",
+           "gdn_status_string", "gdn_abi_version")
 
 
 class GdnError(RuntimeError):
@@ -38,7 +39,7 @@ class gdn_pools(C.Structure):
         ("num_layers", C.c_int32), ("num_v_heads", C.c_int32), ("num_k_heads", C.c_int32),
         ("head_k_dim", C.c_int32), ("head_v_dim", C.c_int32), ("state_dtype", C.c_int32),
         ("num_state_slots", C.c_int32), ("num_rec_slots", C.c_int32),
-        ("rec_tokens", C.c_int32), ("reserved", C.c_int32),
+        ("rec_tokens", C.c_int32), ("record_kind", C.c_int32),
         ("state", C.c_void_p * GDN_MAX_LAYERS), ("rec", C.c_void_p * GDN_MAX_LAYERS),
     ]
 
@@ -92,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
         getattr(lib, name).restype = C.c_int32
     lib.gdn_rec_stride.argtypes = [i32]
     lib.gdn_rec_stride.restype = C.c_int64
+    lib.gdn_record_stride.argtypes = [i32, i32]
+    lib.gdn_record_stride.restype = C.c_int64
     lib.gdn_status_string.argtypes = [i32]
     lib.gdn_status_string.restype = C.c_char_p
     _lib = lib
@@ -104,9 +107,9 @@ def _check(status: int) -> int:
     return status
 
 
-def rec_stride(rec_tokens: int) -> int:
+def rec_stride(rec_tokens: int, record_kind: int = RECORD_CORRECTION) -> int:
     """Floats per (record slot, value head) block, from the library."""
-    return int(load_library().gdn_rec_stride(rec_tokens))
+    return int(load_library().gdn_record_stride(rec_tokens, record_kind))
 
 
 def _ptr(t: torch.Tensor | None):
@@ -135,7 +138,8 @@ class Pools:
     with stride = rec_stride(rec_tokens).
     """
 
-    def __init__(self, state, rec, num_k_heads: int, rec_tokens: int):
+    def __init__(self, state, rec, num_k_heads: int, rec_tokens: int,
+                 record_kind: int = RECORD_CORRECTION):
         self.state = list(state) if not torch.is_tensor(state) else [state[i] for i in range(state.shape[0])]
         self.rec = list(rec) if not torch.is_tensor(rec) else [rec[i] for i in range(rec.shape[0])]
         s0 = self.state[0]
@@ -157,6 +161,8 @@ class Pools:
         st.num_state_slots = self.num_slots
         st.num_rec_slots = self.num_rec_slots
         st.rec_tokens = rec_tokens
+        st.record_kind = record_kind
+        self.record_kind = record_kind
         for i, (s, r) in enumerate(zip(self.state, self.rec)):
             if not (s.is_contiguous() and r.is_contiguous()):
                 raise TypeError("pools must be contiguous")
@@ -165,8 +171,9 @@ class Pools:
         self.c = st
 
     @staticmethod
-    def alloc_records(num_layers, num_rec_slots, hv, rec_tokens, device="cuda"):
-        return torch.zeros((num_layers, num_rec_slots, hv, rec_stride(rec_tokens)),
+    def alloc_records(num_layers, num_rec_slots, hv, rec_tokens, device="cuda",
+                      record_kind=RECORD_CORRECTION):
+        return torch.zeros((num_layers, num_rec_slots, hv, rec_stride(rec_tokens, record_kind)),
                            dtype=torch.float32, device=device)
 
 

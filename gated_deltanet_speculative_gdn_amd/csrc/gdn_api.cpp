@@ -27,6 +27,8 @@ int32_t check_pools(const gdn_pools* p)
     if (p->state_dtype != GDN_STATE_F32 && p->state_dtype != GDN_STATE_BF16) return GDN_ERR_DTYPE;
     if (p->num_state_slots < 1 || p->num_rec_slots < 1) return GDN_ERR_SHAPE;
     if (p->rec_tokens < 1 || p->rec_tokens > GDN_MAX_REC_TOKENS) return GDN_ERR_SHAPE;
+    if (p->record_kind != GDN_RECORD_CORRECTION && p->record_kind != GDN_RECORD_PAYLOAD)
+        return GDN_ERR_SHAPE;
     return GDN_OK;
 }
 
@@ -111,6 +113,15 @@ int64_t gdn_rec_stride(int32_t rec_tokens)
     return (int64_t)rec_tokens * (2 * GDN_HEAD_DIM) + (((int64_t)rec_tokens + 3) & ~(int64_t)3);
 }
 
+int64_t gdn_record_stride(int32_t rec_tokens, int32_t record_kind)
+{
+    if (rec_tokens < 1) return 0;
+    if (record_kind == GDN_RECORD_CORRECTION) return gdn_rec_stride(rec_tokens);
+    if (record_kind != GDN_RECORD_PAYLOAD) return 0;
+    const int64_t bytes = (int64_t)rec_tokens * (2 * GDN_HEAD_DIM * 2 + 8);
+    return ((bytes + 15) & ~(int64_t)15) / 4;
+}
+
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 const char* gdn_status_string(int32_t s)
@@ -139,19 +150,21 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     if ((st = check_layer_ptrs(pools, layer, true))) return st;
     if ((st = check_io(io))) return st;
     if (!state_slot || !rec_slot || !tok_start || !win_len) return GDN_ERR_NULL;
+    if (rec_base && pools->record_kind == GDN_RECORD_PAYLOAD) return GDN_ERR_SHAPE;
     if (num_rows == 0) return GDN_OK;
 
     VerifyParams v;
     memset(&v, 0, sizeof(v));
     v.state = pools->state[layer];
     v.rec = pools->rec[layer];
+    v.payload = pools->record_kind == GDN_RECORD_PAYLOAD;
     v.state_slot = state_slot;
     v.rec_slot = rec_slot;
     v.tok_start = tok_start;
     v.win_len = win_len;
     v.rec_base = rec_base;
     fill_io(v, io);
-    v.rec_stride = gdn_rec_stride(pools->rec_tokens);
+    v.rec_stride = gdn_record_stride(pools->rec_tokens, pools->record_kind);
     v.err = err_flags;
     v.num_rows = num_rows;
     v.hv = pools->num_v_heads;
@@ -247,7 +260,8 @@ int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools*
             c.rec[l] = pools->rec[l];
         }
         c.rec_slot = rec_slot;
-        c.rec_stride = gdn_rec_stride(pools->rec_tokens);
+        c.rec_stride = gdn_record_stride(pools->rec_tokens, pools->record_kind);
+        c.payload = pools->record_kind == GDN_RECORD_PAYLOAD;
         c.hv = pools->num_v_heads;
         c.num_slots = pools->num_state_slots;
         c.num_rec_slots = pools->num_rec_slots;

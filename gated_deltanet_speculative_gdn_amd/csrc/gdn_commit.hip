@@ -169,7 +169,7 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
     }
 }
 
-template <typename StateT, bool ALIGN, int SPLIT, bool NT, bool CONV>
+template <typename StateT, bool ALIGN, int SPLIT, bool NT, bool CONV, bool PAY>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
     if constexpr (CONV) {
@@ -182,9 +182,9 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     constexpr int kRows = kDim / SPLIT;   // rows of the head this workgroup owns
     extern __shared__ float lds[];
     const int T = p.T;
-    float* d_l = lds;                 // [n][kRows] corrections of the owned rows
+    float* d_l = lds;                 // [n][kRows] corrections (payload: values) of the owned rows
     float* k_l = lds + T * kDim;      // [n][128] normalised keys
-    float* g_l = lds + 2 * T * kDim;  // [n] decays
+    float* g_l = lds + 2 * T * kDim;  // [n] decays (payload: then [n] write strengths)
 
     // logical id: (layer, row, value head, part), XCD-contiguous
     const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, p.ssm_wgs) : blockIdx.x;
@@ -221,9 +221,93 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     f32x4 h[IO::kPer];
     IO::template load<NT>(pool + src * slot_elems + head_off, part, t, h);
 
-    // ---- the n records into LDS (own rows of the corrections, all of the keys) ----
     const float* recb = p.rec[layer] + ((int64_t)rs * p.hv + hv) * p.rec_stride;
     constexpr int kRow4 = kRows / 4;
+    f32x4 hb[ALIGN ? IO::kPer : 1];
+    const int c0 = IO::col0(t);
+    if constexpr (PAY) {
+        // ---- payload records: normalise the raw keys (the same helper as
+        // verify, so the same bits), widen the owned rows of the values ----
+        const uint16_t* kb = reinterpret_cast<const uint16_t*>(recb);
+        const uint16_t* vb = kb + (int64_t)T * kDim;
+        float* b_l = g_l + T;             // [n] write strengths
+        for (int job = t >> 4; job < n; job += kThreads / 16) {
+            const int col = 8 * (t & 15);
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + job * kDim + col);
+            float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                          bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+            l2norm_row16(x);
+            st4(k_l + job * kDim + col, f32x4{x[0], x[1], x[2], x[3]});
+            st4(k_l + job * kDim + col + 4, f32x4{x[4], x[5], x[6], x[7]});
+        }
+        for (int i = t; i < n * kRow4; i += kThreads) {
+            const int tt = i / kRow4;
+            const u32x2 raw = *reinterpret_cast<const u32x2*>(vb + tt * kDim + part * kRows +
+                                                              4 * (i - tt * kRow4));
+            st4(d_l + 4 * i, f32x4{bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)});
+        }
+        if (t < n) {
+            g_l[t] = recb[(int64_t)T * kDim + t];
+            b_l[t] = recb[(int64_t)T * (kDim + 1) + t];
+        }
+        __syncthreads();
+
+        // ---- replay with recomputed corrections: h' = g h, u = h' k_hat (a
+        // row reduction over the row's 32 (fp32) or 16 (bf16) lanes),
+        // delta = beta (v - u), h = fma(delta, k_hat, h') ----
+        for (int tt = 0; tt < n; ++tt) {
+            const float g = g_l[tt], be = b_l[tt];
+            if constexpr (sizeof(StateT) == 4) {
+                const f32x4 kh = ld4(k_l + tt * kDim + c0);
+#pragma unroll
+                for (int i = 0; i < IO::kPer; ++i) {
+                    f32x4 hp;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hp[e] = h[i][e] * g;
+                        acc = __builtin_fmaf(hp[e], kh[e], acc);
+                    }
+                    const float u = sum32(acc);
+                    const float d = be * (d_l[tt * kRows + IO::local_row(t, i)] - u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], hp[e]);
+                }
+            } else {
+                const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
+                const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
+#pragma unroll
+                for (int i = 0; i < IO::kPer / 2; ++i) {
+                    f32x4 hp0, hp1;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hp0[e] = h[2 * i][e] * g;
+                        acc = __builtin_fmaf(hp0[e], kh0[e], acc);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hp1[e] = h[2 * i + 1][e] * g;
+                        acc = __builtin_fmaf(hp1[e], kh1[e], acc);
+                    }
+                    const float u = sum16(acc);
+                    const float d = be * (d_l[tt * kRows + IO::local_row(t, i)] - u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[2 * i][e] = __builtin_fmaf(d, kh0[e], hp0[e]);
+                        h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], hp1[e]);
+                    }
+                }
+            }
+            if constexpr (ALIGN) {
+                if (tt + 1 == bl) {
+#pragma unroll
+                    for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
+                }
+            }
+        }
+    } else {
+    // ---- the n records into LDS (own rows of the corrections, all of the keys) ----
     for (int i = t; i < n * kRow4; i += kThreads) {
         const int tt = i / kRow4;
         st4(d_l + 4 * i, ld4(recb + tt * kDim + part * kRows + 4 * (i - tt * kRow4)));
@@ -234,8 +318,6 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     __syncthreads();
 
     // ---- replay: h = fma(delta_t[row], k_hat_t[col], h * g_t) ----
-    f32x4 hb[ALIGN ? IO::kPer : 1];
-    const int c0 = IO::col0(t);
     for (int tt = 0; tt < n; ++tt) {
         const float g = g_l[tt];
         if constexpr (sizeof(StateT) == 4) {
@@ -265,6 +347,7 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                 for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
             }
         }
+    }
     }
 
     // ---- final state first, then the boundary state ----
@@ -313,9 +396,13 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
     void* kargs[] = {&args};
     args.ssm_wgs = p.hv > 0 ? (int64_t)p.num_layers * p.num_rows * p.hv * SPLIT : 0;
     const uint64_t grid = (uint64_t)(args.ssm_wgs + p.conv_wgs);
-    const void* fn = p.conv_wgs > 0
-        ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true>)
-        : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false>);
+    const void* fn =
+        p.payload ? (p.conv_wgs > 0
+                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true, true>)
+                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false, true>))
+                  : (p.conv_wgs > 0
+                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true, false>)
+                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
 }
 
@@ -329,15 +416,12 @@ hipError_t launch_c_dtype(const CommitParams& p, bool bf16_state, hipStream_t s)
 template <bool ALIGN>
 hipError_t launch_c_shape(const CommitParams& p, bool bf16_state, int split, bool nt, hipStream_t s)
 {
-    switch (split * 2 + (nt ? 1 : 0)) {
-    case 2: return launch_c_dtype<ALIGN, 1, false>(p, bf16_state, s);
-    case 3: return launch_c_dtype<ALIGN, 1, true>(p, bf16_state, s);
-    case 4: return launch_c_dtype<ALIGN, 2, false>(p, bf16_state, s);
-    case 5: return launch_c_dtype<ALIGN, 2, true>(p, bf16_state, s);
-    case 8: return launch_c_dtype<ALIGN, 4, false>(p, bf16_state, s);
-    case 9: return launch_c_dtype<ALIGN, 4, true>(p, bf16_state, s);
-    case 16: return launch_c_dtype<ALIGN, 8, false>(p, bf16_state, s);
-    case 17: return launch_c_dtype<ALIGN, 8, true>(p, bf16_state, s);
+    if (!nt) return hipErrorInvalidValue;   // cached state streams measured slower; not built
+    switch (split) {
+    case 1: return launch_c_dtype<ALIGN, 1, true>(p, bf16_state, s);
+    case 2: return launch_c_dtype<ALIGN, 2, true>(p, bf16_state, s);
+    case 4: return launch_c_dtype<ALIGN, 4, true>(p, bf16_state, s);
+    case 8: return launch_c_dtype<ALIGN, 8, true>(p, bf16_state, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -69,6 +69,28 @@ __device__ __forceinline__ float sum16(float x) {
     return x + dpp<kDppRowMirror>(x);
 }
 
+// Sum over the 32 lanes 32m..32m+31: the 16-lane sums of the two DPP rows,
+// then one swap of the halves (ds_swizzle, xor 16 within 32 lanes).
+__device__ __forceinline__ float sum32(float x) {
+    x = sum16(x);
+    constexpr int kSwizzleXor16 = 0x401F;    // bit mode: and 0x1f, or 0, xor 0x10
+    return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), kSwizzleXor16));
+}
+
+// L2 normalisation of a 128-vector held as 8 consecutive elements per lane
+// across the 16 lanes of a DPP row: x * (1 / sqrt(sum x^2 + eps)), the sum
+// taken as 8 fmas in the lane and a 16-lane DPP sum. Every kernel that needs a
+// normalised key calls this, so they all produce the same bits.
+__device__ __forceinline__ void l2norm_row16(float (&x)[8]) {
+    float ssq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ssq = __builtin_fmaf(x[i], x[i], ssq);
+    ssq = sum16(ssq);
+    const float inv = 1.0f / __builtin_sqrtf(ssq + kNormEps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = x[i] * inv;
+}
+
 // ---- vector memory ---------------------------------------------------------
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }

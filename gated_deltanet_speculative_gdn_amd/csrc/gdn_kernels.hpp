@@ -33,6 +33,7 @@ struct VerifyParams {
     float scale;
     bool raw_gates;           // gates from raw a, b with A_log, dt_bias
     bool out_bf16;            // outputs rounded to bf16 (nearest even)
+    bool payload;             // payload records (k, v, gate, beta) instead of corrections
 };
 
 // Short-conv state compaction, run by extra workgroups of the commit launch:
@@ -63,6 +64,7 @@ struct CommitParams {
     int32_t* err;
     int64_t rec_stride;
     int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
+    bool payload;             // payload records: the replay recomputes the corrections
     int64_t ssm_wgs;          // workgroups of the state replay (the first ones of the grid)
     int64_t conv_wgs;         // workgroups of the conv compaction (after them; 0 = none)
     ConvParams conv;
@@ -122,6 +124,6 @@ inline size_t verify_lds_bytes(int T)
 {
     return sizeof(float) * (5 * (size_t)T * 128 + 3 * (size_t)T + 2 * (size_t)T * T);
 }
-inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + (size_t)T); }
+inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + 2 * (size_t)T); }
 
 }  // namespace gdn

@@ -245,18 +245,17 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                       bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
         const int off = (j0 + t) * kDim + 8 * lane16;
+        if (!SNAP && lead && p.payload && kind != 0) {
+            // payload record: the raw key (kind 1) or value (kind 2) bits
+            uint16_t* rp = reinterpret_cast<uint16_t*>(recb) + (kind == 2 ? (int64_t)T * kDim : 0) + off;
+            *reinterpret_cast<u32x4*>(rp) = raw;
+        }
         if (kind == 2) {
             st4(L.vd + off, f32x4{x[0], x[1], x[2], x[3]});
             st4(L.vd + off + 4, f32x4{x[4], x[5], x[6], x[7]});
             continue;
         }
-        float ssq = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ssq = __builtin_fmaf(x[i], x[i], ssq);
-        ssq = sum16(ssq);
-        const float inv = 1.0f / __builtin_sqrtf(ssq + kNormEps);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = x[i] * inv;
+        l2norm_row16(x);
         if (kind == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = x[i] * p.scale;
@@ -265,7 +264,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         } else {
             st4(L.khat + off, f32x4{x[0], x[1], x[2], x[3]});
             st4(L.khat + off + 4, f32x4{x[4], x[5], x[6], x[7]});
-            if (!SNAP && lead) {
+            if (!SNAP && lead && !p.payload) {
                 float* rk = recb + (int64_t)T * kDim + off;
                 st4(rk, f32x4{x[0], x[1], x[2], x[3]});
                 st4(rk + 4, f32x4{x[4], x[5], x[6], x[7]});
@@ -292,7 +291,14 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         }
         L.g[j0 + t] = g;
         L.be[j0 + t] = be;
-        if (!SNAP && lead) recb[2 * (int64_t)T * kDim + j0 + t] = g;
+        if (!SNAP && lead) {
+            if (p.payload) {      // gate and beta after the bf16 key and value fields
+                recb[(int64_t)T * kDim + j0 + t] = g;
+                recb[(int64_t)T * (kDim + 1) + j0 + t] = be;
+            } else {
+                recb[2 * (int64_t)T * kDim + j0 + t] = g;
+            }
+        }
     }
     __syncthreads();
 
@@ -385,7 +391,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
                     u32x2{pack_bf16(ov.x, ov.y), pack_bf16(ov.z, ov.w)};
             else
                 st4(static_cast<float*>(p.out) + oo, ov);
-            if constexpr (!SNAP) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kDim + row0 + c));
+            if (!SNAP && !p.payload) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kDim + row0 + c));
         }
     }
 

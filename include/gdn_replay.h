@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 #define GDN_MAX_LAYERS 64      /* layers per pool set */
 #define GDN_HEAD_DIM 128       /* K = V = 128 */
 #define GDN_MAX_REC_TOKENS 16  /* record capacity T per row */
@@ -70,6 +70,7 @@ typedef enum {
 
 typedef enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 } gdn_state_dtype;
 typedef enum { GDN_GATE_LOG = 0, GDN_GATE_RAW = 1 } gdn_gate_mode;
+typedef enum { GDN_RECORD_CORRECTION = 0, GDN_RECORD_PAYLOAD = 1 } gdn_record_kind;
 typedef enum { GDN_OUT_F32 = 0, GDN_OUT_BF16 = 1 } gdn_out_dtype;
 
 /* Device row-error bits (OR'ed into *err_flags). */
@@ -90,11 +91,18 @@ enum {
  * state[l]: device, layer l's checkpoint pool, [num_state_slots][HV][V][K],
  *   K contiguous, fp32 or bf16 per state_dtype. 16-byte aligned.
  * rec[l]: device, layer l's record pool, [num_rec_slots][HV][rec_stride]
- *   fp32 with rec_stride = gdn_rec_stride(rec_tokens). The block of one
- *   (record slot, value head) is
- *     delta[T][V] | k_hat[T][K] | gate[T] | zero padding to 4 floats,
- *   position p of the window (ring position in ring mode) at index p.
- *   16-byte aligned. Records live only from a step's verify to its commit.
+ *   floats with rec_stride = gdn_record_stride(rec_tokens, record_kind).
+ *   Position p of the window (ring position in ring mode) is at index p of
+ *   each field. 16-byte aligned. Records live only from a step's verify to
+ *   its commit. The block of one (record slot, value head) is
+ *   GDN_RECORD_CORRECTION ([vLLM] Purpose), all fp32:
+ *     delta[T][V] | k_hat[T][K] | gate[T] | padding to 4 floats;
+ *   GDN_RECORD_PAYLOAD (the raw-input record of [TS] Motivation: the commit
+ *     recomputes the corrections, reductions included):
+ *     k[T][K] bf16 (the key head's raw key) | v[T][V] bf16 | gate[T] fp32 |
+ *     beta[T] fp32 | padding to 16 bytes.
+ *   The payload record cannot serve ring mode (pending records would need
+ *   their corrections), so verify rejects a rec_base with it.
  */
 typedef struct gdn_pools {
     int32_t num_layers;       /* 1..GDN_MAX_LAYERS */
@@ -106,7 +114,7 @@ typedef struct gdn_pools {
     int32_t num_state_slots;  /* >= 1 */
     int32_t num_rec_slots;    /* >= 1 */
     int32_t rec_tokens;       /* T, 1..GDN_MAX_REC_TOKENS */
-    int32_t reserved;         /* set to 0 */
+    int32_t record_kind;      /* gdn_record_kind */
     void* state[GDN_MAX_LAYERS];
     float* rec[GDN_MAX_LAYERS];
 } gdn_pools;
@@ -161,8 +169,9 @@ typedef struct gdn_verify_io {
  *   exactly), first replays the rec_base[b] records already at positions
  *   0..rec_base-1 of record slot rec_slot[b] (ring mode, [LMD]; rec_base may
  *   be NULL = all zero), then runs tokens tok_start[b] .. tok_start[b]+w-1:
- *   writes o_t into io->out and the record (delta, k_hat, gate) at position
- *   rec_base + t. The state pool is never written.
+ *   writes o_t into io->out and the record (delta, k_hat, gate; or with the
+ *   payload record kind k, v, gate, beta) at position rec_base + t. The
+ *   state pool is never written.
  * Errors: GDN_ERR_* as in the conventions; device rows with a bad slot,
  * window or record slot are skipped with GDN_ROW_SLOT / _WIN / _REC.
  */
@@ -307,8 +316,14 @@ int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers,
                           int32_t num_rows, const int32_t* dst_slot,
                           const int32_t* n_accept, int32_t* err_flags, void* stream);
 
-/* Floats per (record slot, value head) block: T*(V+K) + T rounded up to 4. */
+/* Floats per (record slot, value head) block of a correction record:
+ * T*(V+K) + T rounded up to 4 (0 for T < 1). */
 int64_t gdn_rec_stride(int32_t rec_tokens);
+
+/* Floats per (record slot, value head) block of either record kind
+ * (payload: (T*(K+V)*2 + 8*T) bytes rounded up to 16, in floats); 0 for
+ * T < 1 or an unknown kind. */
+int64_t gdn_record_stride(int32_t rec_tokens, int32_t record_kind);
 
 const char* gdn_status_string(int32_t status);
 int32_t gdn_abi_version(void);

@@ -16,12 +16,13 @@ def dev_i32(x) -> torch.Tensor:
 
 
 class Harness:
-    def __init__(self, wl, rec_fill=NAN):
+    def __init__(self, wl, rec_fill=NAN, record_kind=G.RECORD_CORRECTION):
         s = wl.spec
         self.wl, self.s = wl, s
-        self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens)
+        self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens,
+                                         record_kind=record_kind)
         self.rec.fill_(rec_fill)          # a record never written stays NaN
-        self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens)
+        self.pools = G.Pools(wl.state, self.rec, s.hk, s.rec_tokens, record_kind)
         self.out = torch.full((s.layers, wl.tokens, s.hv, s.dv), NAN, device="cuda")
         self.err = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.state_slot = dev_i32(wl.state_slot)

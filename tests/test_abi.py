@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.gdn_status_string(s), bytes)
     assert lib.gdn_status_string(-4).decode().startswith("a pointer or stride")
@@ -52,6 +52,16 @@ def test_record_stride():
     assert g.rec_stride(1) == 256 + 4
     assert g.rec_stride(5) == 5 * 256 + 8
     assert g.rec_stride(0) == 0
+
+
+def test_payload_record_stride(lib):
+    # k, v bf16 [T][128] each, gate and beta fp32 [T]: 520 bytes a token, padded to 16 bytes
+    assert lib.gdn_record_stride(4, 1) == 4 * 520 // 4
+    assert lib.gdn_record_stride(1, 1) == 528 // 4
+    assert lib.gdn_record_stride(16, 1) == 16 * 520 // 4
+    assert lib.gdn_record_stride(4, 0) == lib.gdn_rec_stride(4)
+    assert lib.gdn_record_stride(4, 2) == 0
+    assert lib.gdn_record_stride(0, 1) == 0
 
 
 def good_pools():
@@ -100,6 +110,7 @@ def test_verify_zero_rows_is_ok_without_launch(lib):
     (lambda p, io: setattr(p, "rec_tokens", 17), E_SHAPE),
     (lambda p, io: setattr(p, "num_state_slots", 0), E_SHAPE),
     (lambda p, io: setattr(p, "state_dtype", 2), E_DTYPE),
+    (lambda p, io: setattr(p, "record_kind", 2), E_SHAPE),
     (lambda p, io: p.state.__setitem__(0, 0), E_NULL),
     (lambda p, io: p.rec.__setitem__(0, 0), E_NULL),
     (lambda p, io: p.state.__setitem__(0, 0x10004), E_ALIGN),
@@ -134,6 +145,14 @@ def test_verify_accepts_raw_gates_and_bf16_out(lib):
     io.gate_mode, io.A_log, io.dt_bias = 1, 0x90000, 0x90100
     io.out_dtype, io.out = 1, 0x80008          # bf16 output: 8-byte pieces
     assert verify(lib, good_pools(), io, rows=0) == OK
+
+
+def test_payload_records_reject_a_ring_base(lib):
+    p = good_pools()
+    p.record_kind = 1
+    assert lib.gdn_verify(C.byref(p), 0, 4, ROWS, ROWS, ROWS, ROWS, ROWS, C.byref(good_io()),
+                          None, None) == E_SHAPE
+    assert verify(lib, p, good_io(), rows=0) == OK
 
 
 def test_verify_rejects_bad_layer_and_rows(lib):
