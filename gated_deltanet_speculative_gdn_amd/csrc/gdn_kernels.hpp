@@ -34,6 +34,7 @@ struct VerifyParams {
     bool raw_gates;           // gates from raw a, b with A_log, dt_bias
     bool out_bf16;            // outputs rounded to bf16 (nearest even)
     bool payload;             // payload records (k, v, gate, beta) instead of corrections
+    int32_t lds_floor;        // launch: at least this much dynamic LDS (bytes; 0 = the default)
 };
 
 // Short-conv state compaction, run by extra workgroups of the commit launch:
@@ -99,6 +100,11 @@ constexpr int kMaxRecTokens = GDN_MAX_REC_TOKENS;
 // threads per workgroup (256 or 512); a workgroup covers threads/8 * R rows.
 constexpr int kVerifyRowsPerThread = 2;
 constexpr int kVerifyThreads = 256;
+// Verify on fp32 pools with short windows (T <= 4) asks for at least this much
+// dynamic LDS: it then runs six workgroups per CU, set by LDS rather than by
+// registers, which measured 2% faster (sweep of 0..34 KiB); bf16 pools run
+// best without a floor.
+constexpr int kVerifyLdsFloorF32 = 24 << 10;
 // Commit: workgroups per head (1, 2, 4 or 8) for fp32 and bf16 pools (16 KiB
 // per workgroup streams best for fp32, a whole 32 KiB head for bf16); whether
 // state loads and stores are nontemporal; whether workgroup ids are remapped

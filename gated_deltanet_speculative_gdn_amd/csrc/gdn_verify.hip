@@ -154,15 +154,19 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     const bool lead = chunk == 0;
 
     // ---- row decode: a null slot or an empty window is padding ----
+    // (all of the row's metadata is requested before the first wait: one round trip)
     const int slot = ld_uniform(p.state_slot, b);
     const int w = ld_uniform(p.win_len, b);
-    if (slot < 0 || w == 0) return;
     const int ts = ld_uniform(p.tok_start, b);
     int j0 = 0, rs = 0;
     if constexpr (!SNAP) {
         j0 = p.rec_base ? ld_uniform(p.rec_base, b) : 0;
         rs = ld_uniform(p.rec_slot, b);
     }
+    // consume every value here, so the compiler does not sink the later loads
+    // past the padding test into further round trips
+    __asm__ volatile("" ::"s"(ts), "s"(j0), "s"(rs));
+    if (slot < 0 || w == 0) return;
     int err = 0;
     if (slot >= p.num_slots) err |= kRowSlot;
     if (w < 0 || j0 < 0 || (int64_t)j0 + w > T || ts < 0 || (int64_t)ts + w > p.num_tokens)
@@ -306,6 +310,12 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     // Window position p has 2p + 1 dot-product jobs: (k_j . k_p) for j < p, then
     // (k_j . q_p) for j <= p; jobs of p start at p^2 - j0^2.
     const int njobs = P * P - j0 * j0;
+    float gv[TT];                         // the decays, read from LDS once, independently
+#pragma unroll
+    for (int m = 0; m < TT; m += 4) {
+        const f32x4 g4 = ld4(L.g + m);
+        gv[m] = g4.x; gv[m + 1] = g4.y; gv[m + 2] = g4.z; gv[m + 3] = g4.w;
+    }
     for (int jb = tid >> 4; jb < njobs; jb += NT / 16) {
         int pp = j0;
         while ((pp + 1) * (pp + 1) - j0 * j0 <= jb) ++pp;
@@ -321,13 +331,17 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 #pragma unroll
         for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a1[e], c1[e], dot);
         dot = sum16(dot);
-        float gam = 1.f;
-        for (int m = j + 1; m <= pp; ++m) gam = gam * L.g[m];
+        float gam = 1.f;                  // g_{j+1} ... g_pp, in that order
+#pragma unroll
+        for (int m = 1; m < TT; ++m)
+            if (m > j && m <= pp) gam = gam * gv[m];
         if (lane16 == 0) (is_q ? L.cb : L.ca)[j * TT + pp] = gam * dot;
     }
     for (int t = tid; t < w; t += NT) {
-        float gam = 1.f;
-        for (int m = 0; m <= j0 + t; ++m) gam = gam * L.g[m];
+        float gam = 1.f;                  // g_0 ... g_{j0+t}, in that order
+#pragma unroll
+        for (int m = 0; m < TT; ++m)
+            if (m <= j0 + t) gam = gam * gv[m];
         L.g0[j0 + t] = gam;
     }
     __syncthreads();
@@ -425,8 +439,9 @@ hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
+    const size_t lds = verify_lds_bytes(TT) > (size_t)p.lds_floor ? verify_lds_bytes(TT) : (size_t)p.lds_floor;
     return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT>),
-                           dim3(grid), dim3(NT), kargs, verify_lds_bytes(TT), s);
+                           dim3(grid), dim3(NT), kargs, lds, s);
 }
 
 // The smallest compile-time window capacity that holds the record capacity.
