@@ -77,6 +77,13 @@ class Step:
         self.win = i32(wl.win_len)
         self.n = i32(wl.n_accept)
         self.snaps = None
+        self.plan = None
+        if s.ring_steps:
+            # align-mode slots of the ring's flush, planned once on the device
+            self.plan = [torch.empty(s.rows, dtype=torch.int32, device="cuda") for _ in range(4)]
+            G.gdn_align_plan(i32(wl.p0), self.n, i32(wl.block_table), s.block, s.rec_tokens,
+                             *self.plan, err_flags=self.err)
+            self.ring_base = [i32(np.full(s.rows, j)) for j in range(s.ring_steps)]
 
     def gates(self, layer):
         """(a, b, keyword arguments) of the layer's verify: log-gate and beta,
@@ -87,14 +94,30 @@ class Step:
         return rg.a[layer], rg.b[layer], {"A_log": rg.A_log[layer], "dt_bias": rg.dt_bias[layer]}
 
     def verify_all(self):
-        wl = self.wl
-        for layer in range(self.s.layers):
+        wl, s = self.wl, self.s
+        if s.ring_steps:
+            # one single-token verify per layer and ring step, pending records first
+            for j in range(s.ring_steps):
+                sl = slice(j * s.rows, (j + 1) * s.rows)
+                for layer in range(s.layers):
+                    a, b, kw = self.gates(layer)
+                    G.gdn_verify(self.pools, layer, self.slot, self.rec_slot, self.tok, self.win,
+                                 self.ring_base[j], wl.q(layer)[sl], wl.k(layer)[sl],
+                                 wl.v(layer)[sl], a[sl], b[sl], self.out[layer, sl],
+                                 err_flags=self.err, **kw)
+            return
+        for layer in range(s.layers):
             a, b, kw = self.gates(layer)
             G.gdn_verify(self.pools, layer, self.slot, self.rec_slot, self.tok, self.win, None,
                          wl.q(layer), wl.k(layer), wl.v(layer), a, b, self.out[layer],
                          err_flags=self.err, **kw)
 
     def commit(self):
+        if self.plan is not None:
+            src, dst, bl, bs = self.plan
+            G.gdn_commit_all_layers(self.pools, src, dst, self.rec_slot, self.n, bl, bs,
+                                    err_flags=self.err)
+            return
         if self.conv is None:
             G.gdn_commit_all_layers(self.pools, self.slot, self.slot, self.rec_slot, self.n,
                                     err_flags=self.err)
@@ -128,11 +151,20 @@ def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_
     real = (wl.state_slot >= 0) & (wl.win_len > 0)
     w = wl.win_len[real].astype(np.int64)
     n = wl.n_accept[real].astype(np.int64)
-    verify_updates = int(s.layers * s.hv * w.sum())
+    steps = max(s.ring_steps, 1)
+    verify_updates = int(s.layers * s.hv * w.sum() * steps)
     commit_updates = int(s.layers * s.hv * n.sum())
     per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + rec_bytes)
     verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok + (s.hv * 8 if raw_gates else 0))
+    if s.ring_steps:
+        # average launch of the ring: step j also reads j pending records per head
+        pending = sum(range(s.ring_steps)) / s.ring_steps
+        verify_bytes_layer += int(real.sum() * s.hv * pending * rec_bytes)
     commit_bytes = int(s.layers * s.hv * ((n > 0).sum() * 2 * sb + n.sum() * rec_bytes))
+    if s.ring_steps:
+        # align flush: a boundary state is written for windows that cross a block
+        t_b = np.where(wl.p0 % s.block == 0, s.block, s.block - wl.p0 % s.block)
+        commit_bytes += int(s.layers * s.hv * (t_b < wl.n_accept).sum() * sb)
     if conv is not None:
         Ls, C = conv.state.shape[2], conv.state.shape[3]
         row = C * conv.state.element_size()
@@ -249,8 +281,8 @@ def main():
               "needs no collective and shards by heads, rows or layers)", file=sys.stderr)
         sys.exit(2)
     spec = W.WORKLOADS[args.workload]
-    if spec.ring_steps:
-        print("the ring workload is a parity case; bench the MTP workloads", file=sys.stderr)
+    if spec.ring_steps and (args.record == "payload" or args.conv):
+        print("the ring workload needs correction records and no conv states", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     G.load_library()
@@ -277,7 +309,8 @@ def main():
         graph.replay()
         st.commit()
     torch.cuda.synchronize()
-    wall, ver_ms, com_ms, graph_ms = timed_loop(args.steps, graph.replay, st.commit, L)
+    launches = L * max(spec.ring_steps, 1)
+    wall, ver_ms, com_ms, graph_ms = timed_loop(args.steps, graph.replay, st.commit, launches)
     assert st.err.item() == 0, f"device row errors {st.err.item()}"
     log(f"step {wall:.3f} ms: verify graph {graph_ms:.3f} ms ({ver_ms * 1e3:.1f} us/layer), "
         f"commit {com_ms * 1e3:.1f} us")
@@ -286,8 +319,17 @@ def main():
     value = updates / (wall / 1e3)
     com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
     ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
-    step_gbs = (L * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
+    step_gbs = (launches * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
     traffic = counters_traffic(acc["commit_bytes_per_launch"])
+    # the dominant kernel of the step: the one with the larger share of its time
+    if com_ms >= graph_ms:
+        roofline = {"bound": "hbm", "kernel": "commit_all_layers", "achieved": com_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": com_gbs / HBM_PEAK_GBS,
+                    "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "kernel": "verify", "achieved": ver_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ver_gbs / HBM_PEAK_GBS,
+                    "traffic": None}
 
     result = {
         "metric": "commit+verify state-updates/s and achieved HBM GB/s (% peak), B=64 D=4 48 layers",
@@ -306,13 +348,11 @@ def main():
                    "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
                    "gating": args.gating, "out_dtype": args.out_dtype, "conv_states": args.conv,
-                   "record": args.record,
+                   "record": args.record, "ring_steps": spec.ring_steps, "block": spec.block,
                    "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
-        "roofline": {"bound": "hbm", "kernel": "commit_all_layers",
-                     "achieved": com_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": com_gbs / HBM_PEAK_GBS, "traffic": traffic},
+        "roofline": roofline,
         "kernels": {
-            "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": L,
+            "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": launches,
                        "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
                        "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
             "commit_all_layers": {"us_per_launch": com_ms * 1e3, "launches_per_step": 1,
@@ -341,7 +381,7 @@ def main():
                                 "us": ms * 1e3, "GB/s": 2 * nbytes / (ms / 1e3) / 1e9}
         del a, b
 
-    if not args.no_native:
+    if not args.no_native and not spec.ring_steps:   # the native window has no ring mode
         native_graph = capture(st.native_all)
         for _ in range(args.warmup):
             native_graph.replay()

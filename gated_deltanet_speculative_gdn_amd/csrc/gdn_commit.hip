@@ -57,6 +57,11 @@ template <int SPLIT> struct HeadIO<float, SPLIT> {
             else st4(head + 4 * piece(part, t, i), h[i]);
         }
     }
+    template <bool NT>
+    __device__ static void store_piece(float* head, int part, int t, int i, const f32x4& x) {
+        if constexpr (NT) st4_nt(head + 4 * piece(part, t, i), x);
+        else st4(head + 4 * piece(part, t, i), x);
+    }
     // row of piece i relative to the workgroup's first row
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 5; }
     __device__ static int col0(int t) { return 4 * (t & 31); }
@@ -87,6 +92,16 @@ template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
             if constexpr (NT) __builtin_nontemporal_store(x, dst);
             else *dst = x;
         }
+    }
+    // one 16-byte piece (eight values, held as the halves a and c)
+    template <bool NT>
+    __device__ static void store_piece(uint16_t* head, int part, int t, int i, const f32x4& a,
+                                       const f32x4& c) {
+        const u32x4 x{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y),
+                      pack_bf16(c.z, c.w)};
+        u32x4* dst = reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i));
+        if constexpr (NT) __builtin_nontemporal_store(x, dst);
+        else *dst = x;
     }
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 4; }
     __device__ static int col0(int t) { return 8 * (t & 15); }
@@ -218,14 +233,37 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     StateT* pool = static_cast<StateT*>(p.state[layer]);
     const int64_t slot_elems = (int64_t)p.hv * kHeadElems;
     const int64_t head_off = (int64_t)hv * kHeadElems;
+    const float* recb = p.rec[layer] + ((int64_t)rs * p.hv + hv) * p.rec_stride;
+    constexpr int kRow4 = kRows / 4;
+    const int c0 = IO::col0(t);
+    // correction records: this thread's share of the n records (own rows of the
+    // corrections, all of the keys, the decays) is loaded before the tile, so
+    // it arrives first (loads complete in issue order)
+    constexpr int kDChunks = (kMaxRecTokens * kRow4 + kThreads - 1) / kThreads;
+    constexpr int kKChunks = (kMaxRecTokens * (kDim / 4) + kThreads - 1) / kThreads;
+    f32x4 rd[kDChunks], rk[kKChunks];
+    float rg = 0.f;
+    if constexpr (!PAY) {
+#pragma unroll
+        for (int q = 0; q < kDChunks; ++q) {
+            const int i = t + q * kThreads;
+            if (i < n * kRow4) {
+                const int tt = i / kRow4;
+                rd[q] = ld4(recb + tt * kDim + part * kRows + 4 * (i - tt * kRow4));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kKChunks; ++q) {
+            const int i = t + q * kThreads;
+            if (i < n * (kDim / 4)) rk[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
+        }
+        if (t < n) rg = recb[2 * (int64_t)T * kDim + t];
+    }
     f32x4 h[IO::kPer];
     IO::template load<NT>(pool + src * slot_elems + head_off, part, t, h);
 
-    const float* recb = p.rec[layer] + ((int64_t)rs * p.hv + hv) * p.rec_stride;
-    constexpr int kRow4 = kRows / 4;
-    f32x4 hb[ALIGN ? IO::kPer : 1];
-    const int c0 = IO::col0(t);
     if constexpr (PAY) {
+        f32x4 hb[ALIGN ? IO::kPer : 1];
         // ---- payload records: normalise the raw keys (the same helper as
         // verify, so the same bits), widen the owned rows of the values ----
         const uint16_t* kb = reinterpret_cast<const uint16_t*>(recb);
@@ -306,54 +344,74 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                 }
             }
         }
+        // ---- final state first, then the boundary state ----
+        IO::template store<NT>(pool + dst * slot_elems + head_off, part, t, h);
+        if constexpr (ALIGN) {
+            if (write_bnd) IO::template store<NT>(pool + bs * slot_elems + head_off, part, t, hb);
+        }
     } else {
-    // ---- the n records into LDS (own rows of the corrections, all of the keys) ----
-    for (int i = t; i < n * kRow4; i += kThreads) {
-        const int tt = i / kRow4;
-        st4(d_l + 4 * i, ld4(recb + tt * kDim + part * kRows + 4 * (i - tt * kRow4)));
+    // ---- the n records into LDS ----
+#pragma unroll
+    for (int q = 0; q < kDChunks; ++q) {
+        const int i = t + q * kThreads;
+        if (i < n * kRow4) st4(d_l + 4 * i, rd[q]);
     }
-    for (int i = t; i < n * (kDim / 4); i += kThreads)
-        st4(k_l + 4 * i, ld4(recb + (int64_t)T * kDim + 4 * i));
-    if (t < n) g_l[t] = recb[2 * (int64_t)T * kDim + t];
+#pragma unroll
+    for (int q = 0; q < kKChunks; ++q) {
+        const int i = t + q * kThreads;
+        if (i < n * (kDim / 4)) st4(k_l + 4 * i, rk[q]);
+    }
+    if (t < n) g_l[t] = rg;
     __syncthreads();
 
-    // ---- replay: h = fma(delta_t[row], k_hat_t[col], h * g_t) ----
-    for (int tt = 0; tt < n; ++tt) {
-        const float g = g_l[tt];
-        if constexpr (sizeof(StateT) == 4) {
-            const f32x4 kh = ld4(k_l + tt * kDim + c0);
+    // ---- replay piece by piece, h = fma(delta_t[row], k_hat_t[col], h * g_t)
+    // for t < n: each piece waits only for its own load, so the replay of the
+    // first pieces overlaps the transfer of the later ones ----
+    f32x4 hb[ALIGN ? IO::kPer : 1];
+    if constexpr (sizeof(StateT) == 4) {
 #pragma unroll
-            for (int i = 0; i < IO::kPer; ++i) {
-                const float d = d_l[tt * kRows + IO::local_row(t, i)];
+        for (int i = 0; i < IO::kPer; ++i) {
+            const int row = IO::local_row(t, i);
+            for (int tt = 0; tt < n; ++tt) {
+                const float g = g_l[tt];
+                const f32x4 kh = ld4(k_l + tt * kDim + c0);
+                const float d = d_l[tt * kRows + row];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * g);
+                if constexpr (ALIGN) {
+                    if (tt + 1 == bl) hb[i] = h[i];
+                }
             }
-        } else {
-            const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
-            const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
+        }
+    } else {
 #pragma unroll
-            for (int i = 0; i < IO::kPer / 2; ++i) {
-                const float d = d_l[tt * kRows + IO::local_row(t, i)];
+        for (int i = 0; i < IO::kPer / 2; ++i) {
+            const int row = IO::local_row(t, i);
+            for (int tt = 0; tt < n; ++tt) {
+                const float g = g_l[tt];
+                const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
+                const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
+                const float d = d_l[tt * kRows + row];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * g);
                     h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * g);
                 }
+                if constexpr (ALIGN) {
+                    if (tt + 1 == bl) {
+                        hb[2 * i] = h[2 * i];
+                        hb[2 * i + 1] = h[2 * i + 1];
+                    }
+                }
             }
         }
-        if constexpr (ALIGN) {
-            if (tt + 1 == bl) {
-#pragma unroll
-                for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
-            }
-        }
-    }
     }
 
     // ---- final state first, then the boundary state ----
     IO::template store<NT>(pool + dst * slot_elems + head_off, part, t, h);
     if constexpr (ALIGN) {
         if (write_bnd) IO::template store<NT>(pool + bs * slot_elems + head_off, part, t, hb);
+    }
     }
 }
 
@@ -447,8 +505,9 @@ hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool alig
 
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s)
 {
-    return launch_commit_shape(p, bf16_state, align, bf16_state ? kCommitSplitBf16 : kCommitSplitF32,
-                               kCommitNontemporal, s);
+    const int split = bf16_state ? kCommitSplitBf16
+                                 : (p.T > 8 ? kCommitSplitF32LongRecords : kCommitSplitF32);
+    return launch_commit_shape(p, bf16_state, align, split, kCommitNontemporal, s);
 }
 
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s)

@@ -110,6 +110,7 @@ constexpr int kVerifyLdsFloorF32 = 24 << 10;
 // state loads and stores are nontemporal; whether workgroup ids are remapped
 // XCD-contiguous.
 constexpr int kCommitSplitF32 = 4;
+constexpr int kCommitSplitF32LongRecords = 2;   // fp32 pools with more than 8 records per row
 constexpr int kCommitSplitBf16 = 1;
 constexpr bool kCommitNontemporal = true;
 constexpr bool kCommitXcdRemap = true;
