@@ -11,19 +11,26 @@
 // "feat: add Qwen3.5 GDN ReplaySSM", Summary and Implementation (one replay
 // launch over all layers; a cooperative block of four warps per 128x128 head).
 //
-// One launch, one workgroup of four wave64s per (layer, row, value head). The
-// workgroup reads its whole source head (64 KiB fp32 / 32 KiB bf16) into
-// registers with fully coalesced 16-byte loads -- thread t owns 16-byte pieces
-// t + 256*i, so each load instruction of the workgroup covers 4 KiB of
-// contiguous memory -- stages the n records in LDS, replays n tokens
-// elementwise (no reductions), then stores the final state and, in align mode,
-// the boundary state kept in a second register tile. State loads and stores
-// are nontemporal (streamed past the caches: nothing here is reused), and the
-// workgroup ids are remapped so that each XCD streams a contiguous range of
-// heads. Because every thread
-// reads all of its source elements before its first store and writes only the
-// elements it read, a destination or boundary slot equal to the source slot is
-// safe; the pages' read-after-overwrite race between programs cannot occur.
+// One launch over (layer, row, value head, part): a head is split over 1, 2 or
+// 4 workgroups of four wave64s, each owning a contiguous run of its rows. A
+// thread first loads its share of the n records (the workgroup's rows of the
+// corrections, all of the keys, the decays), then its 16-byte pieces of the
+// source head -- thread t owns pieces t + 256*i, so each load instruction of
+// the workgroup covers 4 KiB of contiguous memory. Loads complete in issue
+// order, so the records arrive first; they are staged in LDS, and the replay
+// then runs one piece at a time over all n tokens (elementwise, no
+// reductions), each piece waiting only for its own load. The final state is
+// stored, then in align mode the boundary state kept in a second register
+// tile. State loads and stores are nontemporal (streamed past the caches:
+// nothing here is reused), and the workgroup ids are remapped so that each
+// XCD streams a contiguous range of heads. Because every thread reads all of
+// its source elements before its first store and writes only the elements it
+// read, a destination or boundary slot equal to the source slot is safe; the
+// pages' read-after-overwrite race between programs cannot occur.
+//
+// The same launch optionally carries the short conv's state compaction (extra
+// workgroups after the replay's) and serves the payload record kind, whose
+// replay recomputes each correction from the recorded key and value.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 

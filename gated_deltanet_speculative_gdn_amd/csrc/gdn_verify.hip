@@ -22,8 +22,10 @@
 // is the contraction of S0 with the 2w window vectors: 2w fmas per state
 // element instead of the per-token rule's 4w operations, and ring records cost
 // a scalar term each instead of a pass over the head. The 2w-column product is
-// a dense contraction, but at w = 4 it would fill half of an fp32 16x16x4 MFMA
-// and run at the vector-fma rate, so it stays on the vector ALU.
+// a dense contraction; at w = 4 it fills half of an fp32 16x16x4 MFMA, and
+// matrix-core versions of this kernel measured no faster than this one (its
+// time is set by each workgroup's chain of memory latencies, not by the vector
+// ALU), so it stays on the vector ALU.
 //
 // One workgroup of four wave64s per (row, value head, chunk of 32*R head rows);
 // workgroup ids are remapped so that each XCD streams a contiguous stretch of
@@ -32,6 +34,10 @@
 // 128-byte row segment, and a length-128 reduction is 16 fmas in the lane plus
 // a three-step DPP sum over the eight lanes of a row group. The window's
 // vectors and the per-item scalar coefficients are staged in LDS once.
+//
+// Options carried in the parameters: gates formed here from raw projections
+// (A_log, dt_bias), outputs rounded to bf16, and payload records (the raw key
+// and value with the gates) in place of the corrections.
 //
 // The native baseline is the same template with SNAP = true: the same
 // corrections and outputs, bit for bit, then the states S_1..S_w materialised
