@@ -105,13 +105,13 @@ constexpr int kVerifyThreads = 256;
 // registers, which measured 2% faster (sweep of 0..34 KiB); bf16 pools run
 // best without a floor.
 constexpr int kVerifyLdsFloorF32 = 24 << 10;
-// Commit: workgroups per head (1, 2, 4 or 8) for fp32 and bf16 pools (16 KiB
-// per workgroup streams best for fp32, a whole 32 KiB head for bf16); whether
-// state loads and stores are nontemporal; whether workgroup ids are remapped
-// XCD-contiguous.
-constexpr int kCommitSplitF32 = 4;
+// Commit: workgroups per head (1, 2, 4 or 8) for fp32 and bf16 pools (8 KiB
+// per workgroup streams best for fp32 at up to 8 records, 32 KiB at more; 8
+// KiB for bf16); whether state loads and stores are nontemporal; whether
+// workgroup ids are remapped XCD-contiguous.
+constexpr int kCommitSplitF32 = 8;
 constexpr int kCommitSplitF32LongRecords = 2;   // fp32 pools with more than 8 records per row
-constexpr int kCommitSplitBf16 = 1;
+constexpr int kCommitSplitBf16 = 4;
 constexpr bool kCommitNontemporal = true;
 constexpr bool kCommitXcdRemap = true;
 
