@@ -46,10 +46,16 @@ def log(*a):
 
 
 def source_hash() -> str:
+    """Hash of the commit kernel's sources with comments and blank space
+    removed, so that the stored counters stay valid across comment edits."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

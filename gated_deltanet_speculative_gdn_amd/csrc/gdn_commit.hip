@@ -11,8 +11,8 @@
 // "feat: add Qwen3.5 GDN ReplaySSM", Summary and Implementation (one replay
 // launch over all layers; a cooperative block of four warps per 128x128 head).
 //
-// One launch over (layer, row, value head, part): a head is split over 1, 2 or
-// 4 workgroups of four wave64s, each owning a contiguous run of its rows. A
+// One launch over (layer, row, value head, part): a head is split over 1, 2, 4
+// or 8 workgroups of four wave64s, each owning a contiguous run of its rows. A
 // thread first loads its share of the n records (the workgroup's rows of the
 // corrections, all of the keys, the decays), then its 16-byte pieces of the
 // source head -- thread t owns pieces t + 256*i, so each load instruction of
