@@ -240,11 +240,30 @@ def cpu_baseline(wl, acc, target_s=15.0):
         g = OP.gather(wl, layer, real)
         spent += sum(run(g) for _ in range(reps))
     updates = reps * (acc["verify_updates"] + acc["commit_updates"])
+    # one thread, on the first layer only (a bounded sample of the same rule)
+    g = OP.gather(wl, 0, real)
+    t0 = time.perf_counter()
+    oracle.native_heads(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
+                        keep=keep, nthreads=1)
+    one = time.perf_counter() - t0
+    single = (acc["verify_updates"] + acc["commit_updates"]) / s.layers / one
     return {"value": updates / spent, "unit": "state-updates/s", "cores": nthreads,
-            "kind": "oracle", "seconds": round(spent, 3),
+            "kind": "oracle", "seconds": round(spent, 3), "cpu_model": cpu_model(),
+            "single_thread_value": single,
             "sample": f"{reps} passes over one full step of {s.name}: {s.layers} layers x "
                       f"{len(real)} rows x {s.hv} heads, native per-token rule with the accepted "
                       f"state kept"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def counters_traffic(commit_launch_bytes):
