@@ -217,18 +217,27 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     const float alog_in = (p.raw_gates ? p.A_log : p.a_log)[hv];
     const float dtb_in = (p.raw_gates ? p.dt_bias : p.beta)[hv];
     float* recb = nullptr;
-    f32x4 ring_d[2], ring_k[2];
+    // pending ring records (positions 0 .. j0-1): the corrections of the owned
+    // rows (all this workgroup uses) and all of the keys
+    constexpr int kRowQ = kRowsPerWg / 4;
+    constexpr int kRingD = (kMaxRecTokens * kRowQ + NT - 1) / NT;
+    constexpr int kRingK = (kMaxRecTokens * (kDim / 4) + NT - 1) / NT;
+    f32x4 ring_d[kRingD], ring_k[kRingK];
     float ring_g = 0.f;
     if constexpr (!SNAP) {
         recb = p.rec + ((int64_t)rs * p.hv + hv) * p.rec_stride;
-        // pending ring records (positions 0 .. j0-1): at most 2 pieces per thread (T <= 16)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kRingD; ++q) {
             const int i = tid + q * NT;
-            if (i < j0 * (kDim / 4)) {
-                ring_d[q] = ld4(recb + 4 * i);
-                ring_k[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
+            if (i < j0 * kRowQ) {
+                const int t = i / kRowQ;
+                ring_d[q] = ld4(recb + t * kDim + row0 + 4 * (i - t * kRowQ));
             }
+        }
+#pragma unroll
+        for (int q = 0; q < kRingK; ++q) {
+            const int i = tid + q * NT;
+            if (i < j0 * (kDim / 4)) ring_k[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
         }
         if (tid < j0) ring_g = recb[2 * (int64_t)T * kDim + tid];
     }
@@ -239,12 +248,17 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     // ---- stage the window in LDS ----
     if constexpr (!SNAP) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kRingD; ++q) {
             const int i = tid + q * NT;
-            if (i < j0 * (kDim / 4)) {
-                st4(L.vd + 4 * i, ring_d[q]);
-                st4(L.khat + 4 * i, ring_k[q]);
+            if (i < j0 * kRowQ) {
+                const int t = i / kRowQ;
+                st4(L.vd + t * kDim + row0 + 4 * (i - t * kRowQ), ring_d[q]);
             }
+        }
+#pragma unroll
+        for (int q = 0; q < kRingK; ++q) {
+            const int i = tid + q * NT;
+            if (i < j0 * (kDim / 4)) st4(L.khat + 4 * i, ring_k[q]);
         }
         if (tid < j0) L.g[tid] = ring_g;
     }
