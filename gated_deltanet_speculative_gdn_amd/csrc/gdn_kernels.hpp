@@ -126,11 +126,6 @@ hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool alig
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_align_plan(const PlanParams& p, hipStream_t s);
 
-// Dynamic LDS of the verify kernel for record capacity T (bytes).
-inline size_t verify_lds_bytes(int T)
-{
-    return sizeof(float) * (5 * (size_t)T * 128 + 3 * (size_t)T + 2 * (size_t)T * T);
-}
 inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + 2 * (size_t)T); }
 
 }  // namespace gdn

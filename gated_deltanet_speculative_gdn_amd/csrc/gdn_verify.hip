@@ -120,20 +120,24 @@ __device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x,
 }
 
 // LDS layout of one workgroup (floats), TT = compile-time window capacity
-// (>= the record capacity T), so every LDS offset is an immediate:
+// (>= the record capacity T), so every LDS offset is an immediate; RW = the
+// head rows the workgroup owns (row0 .. row0+RW-1):
 //   khat [TT][128]  normalised keys of every position (ring records and window)
-//   vd   [TT][128]  ring positions: recorded corrections; window positions: values
 //   qt   [TT][128]  window positions: normalised, scaled queries
-//   dw   [TT][128]  window positions: the corrections computed here
-//   ob   [TT][128]  window positions: the outputs (written out coalesced at the end)
+//   vd   [TT][RW]   ring positions: recorded corrections; window positions: values
+//   dw   [TT][RW]   window positions: the corrections computed here
+//   ob   [TT][RW]   window positions: the outputs (written out coalesced at the end)
 //   g [TT], be [TT], g0 [TT] = G(0, p+1)
 //   ca [TT][TT] = G(j+1, p+1) (k_j . k_p), j < p;  cb [TT][TT] = G(j+1, p+1) (k_j . q_p), j <= p
-template <int TT> struct Lds {
-    float *khat, *vd, *qt, *dw, *ob, *g, *be, *g0, *ca, *cb;
+// Only the keys and queries are needed whole (the dot products); keeping the
+// row-indexed fields to the owned rows lets more workgroups share a CU at long
+// record capacities.
+template <int TT, int RW> struct Lds {
+    static constexpr size_t kFloats = 2 * TT * kDim + 3 * TT * RW + 3 * TT + 2 * TT * TT;
+    float *khat, *qt, *vd, *dw, *ob, *g, *be, *g0, *ca, *cb;
     __device__ explicit Lds(float* base)
-        : khat(base), vd(base + TT * kDim), qt(base + 2 * TT * kDim), dw(base + 3 * TT * kDim),
-          ob(base + 4 * TT * kDim), g(base + 5 * TT * kDim), be(g + TT), g0(be + TT), ca(g0 + TT),
-          cb(ca + TT * TT) {}
+        : khat(base), qt(base + TT * kDim), vd(base + 2 * TT * kDim), dw(vd + TT * RW),
+          ob(dw + TT * RW), g(ob + TT * RW), be(g + TT), g0(be + TT), ca(g0 + TT), cb(ca + TT * TT) {}
 };
 
 // NT threads per workgroup, R rows of the head per thread: a workgroup covers
@@ -149,7 +153,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     constexpr int kChunks = kDim / kRowsPerWg;
     extern __shared__ float lds_raw[];
     const int T = p.T;   // record capacity (record addressing); T <= TT
-    const Lds<TT> L(lds_raw);
+    const Lds<TT, kRowsPerWg> L(lds_raw);
 
     const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int chunk = (int)(item % kChunks);
@@ -252,7 +256,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             const int i = tid + q * NT;
             if (i < j0 * kRowQ) {
                 const int t = i / kRowQ;
-                st4(L.vd + t * kDim + row0 + 4 * (i - t * kRowQ), ring_d[q]);
+                st4(L.vd + t * kRowsPerWg + 4 * (i - t * kRowQ), ring_d[q]);
             }
         }
 #pragma unroll
@@ -274,9 +278,13 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             uint16_t* rp = reinterpret_cast<uint16_t*>(recb) + (kind == 2 ? (int64_t)T * kDim : 0) + off;
             *reinterpret_cast<u32x4*>(rp) = raw;
         }
-        if (kind == 2) {
-            st4(L.vd + off, f32x4{x[0], x[1], x[2], x[3]});
-            st4(L.vd + off + 4, f32x4{x[4], x[5], x[6], x[7]});
+        if (kind == 2) {          // values: the owned rows only
+            const int c = 8 * lane16 - row0;
+            if (c >= 0 && c < kRowsPerWg) {
+                float* vp = L.vd + (j0 + t) * kRowsPerWg + c;
+                st4(vp, f32x4{x[0], x[1], x[2], x[3]});
+                st4(vp + 4, f32x4{x[4], x[5], x[6], x[7]});
+            }
             continue;
         }
         l2norm_row16(x);
@@ -368,13 +376,13 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 
     // ---- the window, position by position (unrolled over the capacity TT;
     // the corrections of the owned rows stay in registers) ----
-    const int rbase = row0 + R * grp;
+    const int rl = R * grp;           // first owned row of the group, relative to row0
     float dreg[TT][R];
 #pragma unroll
     for (int pp = 0; pp < TT; ++pp) {
         if (pp < j0) {                 // ring position: its recorded correction
 #pragma unroll
-            for (int r = 0; r < R; ++r) dreg[pp][r] = L.vd[pp * kDim + rbase + r];
+            for (int r = 0; r < R; ++r) dreg[pp][r] = L.vd[pp * kRowsPerWg + rl + r];
             continue;
         }
         if (pp >= P) break;
@@ -392,9 +400,9 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         }
         const float be = L.be[pp];
 #pragma unroll
-        for (int r = 0; r < R; ++r) dreg[pp][r] = be * (L.vd[pp * kDim + rbase + r] - u[r]);
+        for (int r = 0; r < R; ++r) dreg[pp][r] = be * (L.vd[pp * kRowsPerWg + rl + r] - u[r]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) L.dw[pp * kDim + rbase + r] = dreg[pp][r];  // same value in all 8 lanes
+        for (int r = 0; r < R; ++r) L.dw[pp * kRowsPerWg + rl + r] = dreg[pp][r];  // same value in all 8 lanes
 
         float pq[R];
         tile_dot<R>(h, L.qt + pp * kDim, lane8, pq);
@@ -408,7 +416,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cf, dreg[j][r], o[r]);
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) L.ob[pp * kDim + rbase + r] = o[r];   // same value in all 8 lanes
+        for (int r = 0; r < R; ++r) L.ob[pp * kRowsPerWg + rl + r] = o[r];   // same value in all 8 lanes
     }
     __syncthreads();
 
@@ -418,14 +426,14 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int i = tid; i < w * kRow4; i += NT) {
             const int t = i / kRow4;
             const int c = 4 * (i - t * kRow4);
-            const f32x4 ov = ld4(L.ob + (j0 + t) * kDim + row0 + c);
+            const f32x4 ov = ld4(L.ob + (j0 + t) * kRowsPerWg + c);
             const int64_t oo = ((int64_t)ts + t) * p.o_ts + (int64_t)hv * p.o_hs + row0 + c;
             if (p.out_bf16)
                 *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) =
                     u32x2{pack_bf16(ov.x, ov.y), pack_bf16(ov.z, ov.w)};
             else
                 st4(static_cast<float*>(p.out) + oo, ov);
-            if (!SNAP && !p.payload) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kDim + row0 + c));
+            if (!SNAP && !p.payload) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kRowsPerWg + c));
         }
     }
 
@@ -459,7 +467,8 @@ hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
-    const size_t lds = verify_lds_bytes(TT) > (size_t)p.lds_floor ? verify_lds_bytes(TT) : (size_t)p.lds_floor;
+    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R>::kFloats;
+    const size_t lds = need > (size_t)p.lds_floor ? need : (size_t)p.lds_floor;
     return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT>),
                            dim3(grid), dim3(NT), kargs, lds, s);
 }
