@@ -1,7 +1,8 @@
-"""GPU parity at the interface's limits: the longest windows (T = 16 records,
-every position in one window), a window placed after pending records (record
-positions 5..15 verified after positions 0..4), windows of 8, and a commit
-over the most layers a pool set may hold (64). Bars as in test_parity_gpu."""
+"""GPU parity at the interface's limits: the longest windows (T = 8 and 16
+records, every position in one window; fp32 and bf16 pools), a window placed
+after pending records (record positions 5..15 verified after positions
+0..4), and a commit over the most layers a pool set may hold (64). Bars as in
+test_parity_gpu."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +15,11 @@ from test_parity_gpu import check_layer, pool_bits
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
 @pytest.mark.parametrize("T", [8, 16])
-def test_longest_windows(gdn, T):
+def test_longest_windows(gdn, T, dtype):
     spec = W.shrink(W.SINGLE_LAYER, rows=8, window=T, rec_tokens=T, n_lo=1, n_hi=T)
-    wl = W.make_workload(spec, device="cuda", seed=80 + T)
+    wl = W.make_workload(spec, device="cuda", seed=80 + T, state_dtype=dtype)
     h = Harness(wl)
     pre = wl.state.clone()
     h.verify_all()

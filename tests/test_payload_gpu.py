@@ -94,10 +94,9 @@ def test_payload_verify_records_and_outputs(gdn):
         assert_bitwise(be, gd["beta"], f"layer {layer} payload write strengths")
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
-def test_payload_commit(gdn, dtype):
-    spec = W.shrink(W.ALL_LAYER, layers=3)
-    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+def _payload_commit(spec, dtype, seed=None):
+    kw = {} if seed is None else {"seed": seed}
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype, **kw)
     h = Harness(wl, record_kind=G.RECORD_PAYLOAD)
     pre = wl.state.clone()
     h.verify_all()
@@ -112,6 +111,19 @@ def test_payload_commit(gdn, dtype):
         got = wl.state[layer].index_select(0, slots).reshape(-1, 128, 128)
         ref = res.kept[np.repeat(live, spec.hv), 0]
         check_states(got, ref, dtype, f"layer {layer} payload-commit states")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_payload_commit(gdn, dtype):
+    _payload_commit(W.shrink(W.ALL_LAYER, layers=3), dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_payload_commit_longest_windows(gdn, dtype):
+    """16 payload records per row (the record capacity's limit), n = 1..16."""
+    T = 16
+    spec = W.shrink(W.SINGLE_LAYER, rows=8, window=T, rec_tokens=T, n_lo=1, n_hi=T)
+    _payload_commit(spec, dtype, seed=96)
 
 
 def test_payload_commit_align(gdn):
