@@ -243,14 +243,35 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     const float* recb = p.rec[layer] + ((int64_t)rs * p.hv + hv) * p.rec_stride;
     constexpr int kRow4 = kRows / 4;
     const int c0 = IO::col0(t);
-    // correction records: this thread's share of the n records (own rows of the
-    // corrections, all of the keys, the decays) is loaded before the tile, so
-    // it arrives first (loads complete in issue order)
+    // Records: this thread's share of the n records is loaded before the tile,
+    // so it arrives first (loads complete in issue order). Correction records:
+    // the owned rows of the corrections, all of the keys, the decays. Payload
+    // records: one 16-byte piece of a raw key, the owned rows of the raw values,
+    // a decay and a write strength.
     constexpr int kDChunks = (kMaxRecTokens * kRow4 + kThreads - 1) / kThreads;
     constexpr int kKChunks = (kMaxRecTokens * (kDim / 4) + kThreads - 1) / kThreads;
     f32x4 rd[kDChunks], rk[kKChunks];
-    float rg = 0.f;
-    if constexpr (!PAY) {
+    float rg = 0.f, rb = 0.f;
+    u32x4 pk = {0u, 0u, 0u, 0u};
+    u32x2 pv[kDChunks];
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(recb);
+    const uint16_t* vb = kb + (int64_t)T * kDim;
+    if constexpr (PAY) {
+        static_assert(kMaxRecTokens * kDim / 8 <= kThreads, "one key piece per thread");
+        if ((t >> 4) < n) pk = *reinterpret_cast<const u32x4*>(kb + (t >> 4) * kDim + 8 * (t & 15));
+#pragma unroll
+        for (int q = 0; q < kDChunks; ++q) {
+            const int i = t + q * kThreads;
+            if (i < n * kRow4) {
+                const int tt = i / kRow4;
+                pv[q] = *reinterpret_cast<const u32x2*>(vb + tt * kDim + part * kRows + 4 * (i - tt * kRow4));
+            }
+        }
+        if (t < n) {
+            rg = recb[(int64_t)T * kDim + t];
+            rb = recb[(int64_t)T * (kDim + 1) + t];
+        }
+    } else {
 #pragma unroll
         for (int q = 0; q < kDChunks; ++q) {
             const int i = t + q * kThreads;
@@ -270,42 +291,42 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     IO::template load<NT>(pool + src * slot_elems + head_off, part, t, h);
 
     if constexpr (PAY) {
-        f32x4 hb[ALIGN ? IO::kPer : 1];
-        // ---- payload records: normalise the raw keys (the same helper as
-        // verify, so the same bits), widen the owned rows of the values ----
-        const uint16_t* kb = reinterpret_cast<const uint16_t*>(recb);
-        const uint16_t* vb = kb + (int64_t)T * kDim;
+        // ---- payload records into LDS: keys normalised with the same helper
+        // as verify (so the same bits), the owned rows of the values widened ----
         float* b_l = g_l + T;             // [n] write strengths
-        for (int job = t >> 4; job < n; job += kThreads / 16) {
-            const int col = 8 * (t & 15);
-            const u32x4 raw = *reinterpret_cast<const u32x4*>(kb + job * kDim + col);
-            float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                          bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+        if ((t >> 4) < n) {               // uniform over each 16-lane row of the reduction
+            float x[8] = {bf16_lo(pk.x), bf16_hi(pk.x), bf16_lo(pk.y), bf16_hi(pk.y),
+                          bf16_lo(pk.z), bf16_hi(pk.z), bf16_lo(pk.w), bf16_hi(pk.w)};
             l2norm_row16(x);
-            st4(k_l + job * kDim + col, f32x4{x[0], x[1], x[2], x[3]});
-            st4(k_l + job * kDim + col + 4, f32x4{x[4], x[5], x[6], x[7]});
+            float* kp = k_l + (t >> 4) * kDim + 8 * (t & 15);
+            st4(kp, f32x4{x[0], x[1], x[2], x[3]});
+            st4(kp + 4, f32x4{x[4], x[5], x[6], x[7]});
         }
-        for (int i = t; i < n * kRow4; i += kThreads) {
-            const int tt = i / kRow4;
-            const u32x2 raw = *reinterpret_cast<const u32x2*>(vb + tt * kDim + part * kRows +
-                                                              4 * (i - tt * kRow4));
-            st4(d_l + 4 * i, f32x4{bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)});
+#pragma unroll
+        for (int q = 0; q < kDChunks; ++q) {
+            const int i = t + q * kThreads;
+            if (i < n * kRow4)
+                st4(d_l + 4 * i, f32x4{bf16_lo(pv[q].x), bf16_hi(pv[q].x), bf16_lo(pv[q].y), bf16_hi(pv[q].y)});
         }
         if (t < n) {
-            g_l[t] = recb[(int64_t)T * kDim + t];
-            b_l[t] = recb[(int64_t)T * (kDim + 1) + t];
+            g_l[t] = rg;
+            b_l[t] = rb;
         }
         __syncthreads();
 
-        // ---- replay with recomputed corrections: h' = g h, u = h' k_hat (a
-        // row reduction over the row's 32 (fp32) or 16 (bf16) lanes),
-        // delta = beta (v - u), h = fma(delta, k_hat, h') ----
-        for (int tt = 0; tt < n; ++tt) {
-            const float g = g_l[tt], be = b_l[tt];
-            if constexpr (sizeof(StateT) == 4) {
-                const f32x4 kh = ld4(k_l + tt * kDim + c0);
+        // ---- replay piece by piece with recomputed corrections: h' = g h,
+        // u = h' k_hat (a reduction over the lanes holding the piece's row: 32
+        // for fp32, 16 for bf16), delta = beta (v - u), h = fma(delta, k_hat, h').
+        // A row lies within one piece index, so each piece waits only for its
+        // own load. ----
+        f32x4 hb[ALIGN ? IO::kPer : 1];
+        if constexpr (sizeof(StateT) == 4) {
 #pragma unroll
-                for (int i = 0; i < IO::kPer; ++i) {
+            for (int i = 0; i < IO::kPer; ++i) {
+                const int row = IO::local_row(t, i);
+                for (int tt = 0; tt < n; ++tt) {
+                    const float g = g_l[tt], be = b_l[tt];
+                    const f32x4 kh = ld4(k_l + tt * kDim + c0);
                     f32x4 hp;
                     float acc = 0.f;
 #pragma unroll
@@ -313,16 +334,22 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                         hp[e] = h[i][e] * g;
                         acc = __builtin_fmaf(hp[e], kh[e], acc);
                     }
-                    const float u = sum32(acc);
-                    const float d = be * (d_l[tt * kRows + IO::local_row(t, i)] - u);
+                    const float d = be * (d_l[tt * kRows + row] - sum32(acc));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], hp[e]);
+                    if constexpr (ALIGN) {
+                        if (tt + 1 == bl) hb[i] = h[i];
+                    }
                 }
-            } else {
-                const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
-                const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
+            }
+        } else {
 #pragma unroll
-                for (int i = 0; i < IO::kPer / 2; ++i) {
+            for (int i = 0; i < IO::kPer / 2; ++i) {
+                const int row = IO::local_row(t, i);
+                for (int tt = 0; tt < n; ++tt) {
+                    const float g = g_l[tt], be = b_l[tt];
+                    const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
+                    const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
                     f32x4 hp0, hp1;
                     float acc = 0.f;
 #pragma unroll
@@ -335,19 +362,18 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                         hp1[e] = h[2 * i + 1][e] * g;
                         acc = __builtin_fmaf(hp1[e], kh1[e], acc);
                     }
-                    const float u = sum16(acc);
-                    const float d = be * (d_l[tt * kRows + IO::local_row(t, i)] - u);
+                    const float d = be * (d_l[tt * kRows + row] - sum16(acc));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         h[2 * i][e] = __builtin_fmaf(d, kh0[e], hp0[e]);
                         h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], hp1[e]);
                     }
-                }
-            }
-            if constexpr (ALIGN) {
-                if (tt + 1 == bl) {
-#pragma unroll
-                    for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
+                    if constexpr (ALIGN) {
+                        if (tt + 1 == bl) {
+                            hb[2 * i] = h[2 * i];
+                            hb[2 * i + 1] = h[2 * i + 1];
+                        }
+                    }
                 }
             }
         }
