@@ -64,11 +64,6 @@ template <int SPLIT> struct HeadIO<float, SPLIT> {
             else st4(head + 4 * piece(part, t, i), h[i]);
         }
     }
-    template <bool NT>
-    __device__ static void store_piece(float* head, int part, int t, int i, const f32x4& x) {
-        if constexpr (NT) st4_nt(head + 4 * piece(part, t, i), x);
-        else st4(head + 4 * piece(part, t, i), x);
-    }
     // row of piece i relative to the workgroup's first row
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 5; }
     __device__ static int col0(int t) { return 4 * (t & 31); }
@@ -99,16 +94,6 @@ template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
             if constexpr (NT) __builtin_nontemporal_store(x, dst);
             else *dst = x;
         }
-    }
-    // one 16-byte piece (eight values, held as the halves a and c)
-    template <bool NT>
-    __device__ static void store_piece(uint16_t* head, int part, int t, int i, const f32x4& a,
-                                       const f32x4& c) {
-        const u32x4 x{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y),
-                      pack_bf16(c.z, c.w)};
-        u32x4* dst = reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i));
-        if constexpr (NT) __builtin_nontemporal_store(x, dst);
-        else *dst = x;
     }
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 4; }
     __device__ static int col0(int t) { return 8 * (t & 15); }
