@@ -1,8 +1,8 @@
 """GPU parity at the interface's limits: the longest windows (T = 8 and 16
 records, every position in one window; fp32 and bf16 pools), a window placed
 after pending records (record positions 5..15 verified after positions
-0..4), and a commit over the most layers a pool set may hold (64). Bars as in
-test_parity_gpu."""
+0..4), a commit over the most layers a pool set may hold (64), and key-head
+group sizes 1 to 12. Bars as in test_parity_gpu."""
 import numpy as np
 import pytest
 import torch
@@ -70,3 +70,19 @@ def test_commit_over_64_layers(gdn):
     assert h.err_value() == 0
     for layer in range(spec.layers):
         check_layer(h, layer, np.arange(spec.rows), wl.n_accept, pre[layer])
+
+
+@pytest.mark.parametrize("hv,hk", [(8, 2), (6, 6), (6, 3), (12, 1)],
+                         ids=["group4", "group1", "hv6_group2", "group12"])
+def test_key_head_groups(gdn, hv, hk):
+    """Value head h reads key head h / (HV/HK) for group sizes 1, 2, 4 and 12,
+    including a head count that is not a power of two; 7 rows on random slots."""
+    spec = W.shrink(W.SINGLE_LAYER, rows=7, hv=hv, hk=hk, num_slots=32, slot_mode="random")
+    wl = W.make_workload(spec, device="cuda", seed=100 + hv * 16 + hk)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    check_layer(h, 0, np.arange(spec.rows), wl.n_accept, pre[0])
