@@ -298,8 +298,10 @@ def main():
                          "q/k/v channels) in the commit launch")
     ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also time a plain device copy of this size (counter calibration)")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="also time a plain device-to-device copy of this size: the measured "
+                         "copy ceiling reported beside the kernels, and the counter calibration "
+                         "(0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
@@ -402,8 +404,10 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 5
-        result["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes,
-                                "us": ms * 1e3, "GB/s": 2 * nbytes / (ms / 1e3) / 1e9}
+        cp_gbs = 2 * nbytes / (ms / 1e3) / 1e9
+        result["copy_probe"] = {"what": "runtime device-to-device copy (read + write bytes)",
+                                "bytes_read": nbytes, "bytes_written": nbytes,
+                                "us": ms * 1e3, "GB/s": cp_gbs, "frac_of_peak": cp_gbs / HBM_PEAK_GBS}
         del a, b
 
     if not args.no_native and not spec.ring_steps:   # the native window has no ring mode
