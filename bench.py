@@ -408,7 +408,47 @@ def main():
         result["copy_probe"] = {"what": "runtime device-to-device copy (read + write bytes)",
                                 "bytes_read": nbytes, "bytes_written": nbytes,
                                 "us": ms * 1e3, "GB/s": cp_gbs, "frac_of_peak": cp_gbs / HBM_PEAK_GBS}
-        del a, b
+        # the library's own probe kernels: the commit's access pattern, read only,
+        # write only and copy
+        sink = torch.empty(nbytes // G.GDN_PROBE_CHUNK * 4, device="cuda")
+        probes = {"read": (G.PROBE_READ, a, sink, nbytes + nbytes // 1024),
+                  "write": (G.PROBE_WRITE, None, b, nbytes),
+                  "copy": (G.PROBE_COPY, a, b, 2 * nbytes)}
+        hp = {"what": "library probe kernels, 16-byte non-temporal pieces, 4 KiB per "
+                      "workgroup instruction, XCD-contiguous ids (bytes read + written)"}
+        for name, (kind, src_t, dst_t, moved) in probes.items():
+            G.gdn_bandwidth_probe(kind, src_t, dst_t, nbytes)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(5):
+                G.gdn_bandwidth_probe(kind, src_t, dst_t, nbytes)
+            e1.record()
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1) / 5
+            gbs = moved / (pms / 1e3) / 1e9
+            hp[name] = {"us": pms * 1e3, "GB/s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+        # read ceiling at the size of one verify launch: launch ramp and drain
+        # weigh more at ~100 MB than at 1 GiB; the reads rotate through the
+        # 1 GiB buffer so that no repetition is served from the 256 MB cache
+        vb = acc["verify_bytes_per_launch"]
+        vn = vb - vb % G.GDN_PROBE_CHUNK
+        if 0 < vn <= nbytes:
+            reps = 10
+            offs = [(i * vn) % (nbytes - vn + 1) // 16 * 16 for i in range(reps)]
+            views = [a.view(torch.uint8)[o:o + vn] for o in offs]
+            G.gdn_bandwidth_probe(G.PROBE_READ, views[0], sink, vn)
+            torch.cuda.synchronize()
+            e0.record()
+            for v_ in views:
+                G.gdn_bandwidth_probe(G.PROBE_READ, v_, sink, vn)
+            e1.record()
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1) / reps
+            gbs = vn / (pms / 1e3) / 1e9
+            hp["read_at_verify_launch_bytes"] = {"bytes": vn, "us": pms * 1e3, "GB/s": gbs,
+                                                 "frac_of_peak": gbs / HBM_PEAK_GBS}
+        result["hbm_probe"] = hp
+        del a, b, sink
 
     if not args.no_native and not spec.ring_steps:   # the native window has no ring mode
         native_graph = capture(st.native_all)

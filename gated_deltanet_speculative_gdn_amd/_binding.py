@@ -1,4 +1,5 @@
-"""ctypes binding of ``libgdnreplay.so`` (the C ABI in include/gdn_replay.h).
+"""ctypes binding of ``libgdnreplay.so`` (the C ABI in include/gdn_replay.h and
+include/gdn_probe.h).
 
 Argument marshalling only: torch tensors are turned into device pointers,
 element strides and the current HIP stream, and every call goes straight to
@@ -22,10 +23,12 @@ GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
 RECORD_CORRECTION, RECORD_PAYLOAD = 0, 1   # gdn_record_kind
 OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
+PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2   # gdn_probe_kind
+GDN_PROBE_CHUNK = 16384
 
 EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv", "gdn_align_plan",
            "gdn_native_window", "gdn_native_accept", "gdn_rec_stride", "gdn_record_stride",
-           "gdn_status_string", "gdn_abi_version")
+           "gdn_status_string", "gdn_abi_version", "gdn_bandwidth_probe")
 
 
 class GdnError(RuntimeError):
@@ -88,8 +91,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.gdn_native_window.argtypes = [P(gdn_pools), i32, i32, vp, vp, vp, P(gdn_verify_io), vp,
                                       vp, vp]
     lib.gdn_native_accept.argtypes = [P(gdn_pools), P(vp), i32, vp, vp, vp, vp]
-    for name in ("gdn_verify", "gdn_commit_all_layers", "gdn_align_plan", "gdn_native_window",
-                 "gdn_native_accept", "gdn_abi_version"):
+    lib.gdn_bandwidth_probe.argtypes = [i32, vp, vp, i64, vp]
+    for name in ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv",
+                 "gdn_align_plan", "gdn_native_window", "gdn_native_accept", "gdn_abi_version",
+                 "gdn_bandwidth_probe"):
         getattr(lib, name).restype = C.c_int32
     lib.gdn_rec_stride.argtypes = [i32]
     lib.gdn_rec_stride.restype = C.c_int64
@@ -316,3 +321,15 @@ def gdn_align_plan(num_computed, n_accept, block_table, block_size: int, max_acc
         max_accept, _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
         _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
         _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+
+
+def gdn_bandwidth_probe(kind: int, src, dst, nbytes: int | None = None, *, stream=None) -> int:
+    """Stream ``nbytes`` (default: the size of ``src``, else of ``dst``) through
+    HBM with the library's read, write or copy probe kernel. ``src`` may be
+    None for PROBE_WRITE; for PROBE_READ ``dst`` receives one 16-byte word per
+    GDN_PROBE_CHUNK bytes."""
+    lib = load_library()
+    if nbytes is None:
+        t = src if src is not None else dst
+        nbytes = t.numel() * t.element_size()
+    return _check(lib.gdn_bandwidth_probe(kind, _ptr(src), _ptr(dst), nbytes, _stream(stream)))

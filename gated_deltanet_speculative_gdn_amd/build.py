@@ -21,7 +21,7 @@ LIB_NAME = "libgdnreplay.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "gdn_verify.hip", "gdn_commit.hip", "gdn_plan.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_verify.hip", "gdn_commit.hip", "gdn_plan.hip", "gdn_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every function
-include/gdn_replay.h declares, and rejects malformed host arguments with the
+include/gdn_replay.h and include/gdn_probe.h declare, and rejects malformed host arguments with the
 documented status before any HIP call (vLLM RecoverSSM PR, Test Plan:
 malformed-input rejection). Only calls that validation rejects are made."""
 import ctypes as C
@@ -248,3 +248,19 @@ def test_commit_conv_validation(lib):
     assert commit_conv(lib, None, c) == E_NULL
     c = good_conv(); c.state[0] = 0xA0008
     assert commit_conv(lib, None, c) == E_ALIGN
+
+
+def test_bandwidth_probe_rejects_bad_arguments(lib):
+    fake = C.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
+    odd = C.c_void_p((1 << 20) + 8)
+    chunk = B.GDN_PROBE_CHUNK
+    assert lib.gdn_bandwidth_probe(3, fake, fake, chunk, None) == E_SHAPE
+    assert lib.gdn_bandwidth_probe(-1, fake, fake, chunk, None) == E_SHAPE
+    assert lib.gdn_bandwidth_probe(B.PROBE_COPY, fake, fake, 0, None) == E_SHAPE
+    assert lib.gdn_bandwidth_probe(B.PROBE_COPY, fake, fake, chunk + 16, None) == E_SHAPE
+    assert lib.gdn_bandwidth_probe(B.PROBE_COPY, fake, fake, chunk * (1 << 31), None) == E_SHAPE
+    assert lib.gdn_bandwidth_probe(B.PROBE_COPY, None, fake, chunk, None) == E_NULL
+    assert lib.gdn_bandwidth_probe(B.PROBE_READ, None, fake, chunk, None) == E_NULL
+    assert lib.gdn_bandwidth_probe(B.PROBE_WRITE, None, None, chunk, None) == E_NULL
+    assert lib.gdn_bandwidth_probe(B.PROBE_COPY, odd, fake, chunk, None) == E_ALIGN
+    assert lib.gdn_bandwidth_probe(B.PROBE_WRITE, None, odd, chunk, None) == E_ALIGN
