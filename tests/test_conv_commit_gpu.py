@@ -47,18 +47,22 @@ def expected_pool(pre_layer, x_layer, rows, src, dst, n, ts, bnd_len=None, bnd_s
     return out
 
 
-@pytest.mark.parametrize("conv_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
-def test_fused_commit_mtp(gdn, conv_dtype):
+@pytest.mark.parametrize("conv_dtype,record_kind",
+                         [(torch.bfloat16, G.RECORD_CORRECTION), (torch.float32, G.RECORD_CORRECTION),
+                          (torch.bfloat16, G.RECORD_PAYLOAD)],
+                         ids=["bf16", "fp32", "bf16-payload-records"])
+def test_fused_commit_mtp(gdn, conv_dtype, record_kind):
     """Three layers of the 16-row workload: verify, then one launch commits the
-    recurrent states and compacts the conv states in place (dst = src)."""
+    recurrent states and compacts the conv states in place (dst = src); with
+    correction and with payload records."""
     spec = W.shrink(W.ALL_LAYER, layers=3)
     wl = W.make_workload(spec, device="cuda")
     cv = W.make_conv(wl, state_len=3, dtype=conv_dtype, device="cuda")
-    h = Harness(wl)
+    h = Harness(wl, record_kind=record_kind)
     h.verify_all()
     torch.cuda.synchronize()
     ref_state = wl.state.clone()
-    ref_pools = G.Pools(ref_state, h.rec, spec.hk, spec.rec_tokens)
+    ref_pools = G.Pools(ref_state, h.rec, spec.hk, spec.rec_tokens, record_kind)
     G.gdn_commit_all_layers(ref_pools, h.state_slot, h.state_slot, h.rec_slot, h.n_accept,
                             err_flags=h.err)
     pre = raw(cv.state)
