@@ -11,8 +11,8 @@
 // "feat: add Qwen3.5 GDN ReplaySSM", Summary and Implementation (one replay
 // launch over all layers; a cooperative block of four warps per 128x128 head).
 //
-// One launch over (layer, row, value head, part): a head is split over 1, 2, 4
-// or 8 workgroups of four wave64s, each owning a contiguous run of its rows. A
+// One launch over (layer, row, value head, part): a head is split over 2, 4 or
+// 8 workgroups of four wave64s, each owning a contiguous run of its rows. A
 // thread first loads its share of the n records (the workgroup's rows of the
 // corrections, all of the keys, the decays), then its 16-byte pieces of the
 // source head -- thread t owns pieces t + 256*i, so each load instruction of
@@ -50,19 +50,13 @@ template <typename StateT, int SPLIT> struct HeadIO;
 template <int SPLIT> struct HeadIO<float, SPLIT> {
     static constexpr int kPer = 16 / SPLIT;              // pieces (f32x4) per thread
     __device__ static int piece(int part, int t, int i) { return part * (4096 / SPLIT) + t + kThreads * i; }
-    template <bool NT>
     __device__ static void load(const float* head, int part, int t, f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            h[i] = NT ? ld4_nt(head + 4 * piece(part, t, i)) : ld4(head + 4 * piece(part, t, i));
+        for (int i = 0; i < kPer; ++i) h[i] = ld4_nt(head + 4 * piece(part, t, i));
     }
-    template <bool NT>
     __device__ static void store(float* head, int part, int t, const f32x4 (&h)[kPer]) {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            if constexpr (NT) st4_nt(head + 4 * piece(part, t, i), h[i]);
-            else st4(head + 4 * piece(part, t, i), h[i]);
-        }
+        for (int i = 0; i < kPer; ++i) st4_nt(head + 4 * piece(part, t, i), h[i]);
     }
     // row of piece i relative to the workgroup's first row
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 5; }
@@ -73,26 +67,22 @@ template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
     static constexpr int kPieces = 8 / SPLIT;            // 16-byte pieces per thread
     static constexpr int kPer = 2 * kPieces;             // held as f32x4 halves
     __device__ static int piece(int part, int t, int i) { return part * (2048 / SPLIT) + t + kThreads * i; }
-    template <bool NT>
     __device__ static void load(const uint16_t* head, int part, int t, f32x4 (&h)[kPer]) {
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
-            const u32x4* q = reinterpret_cast<const u32x4*>(head + 8 * piece(part, t, i));
-            const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
+            const u32x4 x = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(head + 8 * piece(part, t, i)));
             h[2 * i] = f32x4{bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
             h[2 * i + 1] = f32x4{bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
         }
     }
-    template <bool NT>
     __device__ static void store(uint16_t* head, int part, int t, const f32x4 (&h)[kPer]) {
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) {
             const f32x4 a = h[2 * i], c = h[2 * i + 1];
             const u32x4 x{pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(c.x, c.y),
                           pack_bf16(c.z, c.w)};
-            u32x4* dst = reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i));
-            if constexpr (NT) __builtin_nontemporal_store(x, dst);
-            else *dst = x;
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i)));
         }
     }
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 4; }
@@ -176,7 +166,7 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
     }
 }
 
-template <typename StateT, bool ALIGN, int SPLIT, bool NT, bool CONV, bool PAY>
+template <typename StateT, bool ALIGN, int SPLIT, bool CONV, bool PAY>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
     if constexpr (CONV) {
@@ -273,7 +263,7 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         if (t < n) rg = recb[2 * (int64_t)T * kDim + t];
     }
     f32x4 h[IO::kPer];
-    IO::template load<NT>(pool + src * slot_elems + head_off, part, t, h);
+    IO::load(pool + src * slot_elems + head_off, part, t, h);
 
     if constexpr (PAY) {
         // ---- payload records into LDS: keys normalised with the same helper
@@ -363,9 +353,9 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
             }
         }
         // ---- final state first, then the boundary state ----
-        IO::template store<NT>(pool + dst * slot_elems + head_off, part, t, h);
+        IO::store(pool + dst * slot_elems + head_off, part, t, h);
         if constexpr (ALIGN) {
-            if (write_bnd) IO::template store<NT>(pool + bs * slot_elems + head_off, part, t, hb);
+            if (write_bnd) IO::store(pool + bs * slot_elems + head_off, part, t, hb);
         }
     } else {
     // ---- the n records into LDS ----
@@ -426,9 +416,9 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     }
 
     // ---- final state first, then the boundary state ----
-    IO::template store<NT>(pool + dst * slot_elems + head_off, part, t, h);
+    IO::store(pool + dst * slot_elems + head_off, part, t, h);
     if constexpr (ALIGN) {
-        if (write_bnd) IO::template store<NT>(pool + bs * slot_elems + head_off, part, t, hb);
+        if (write_bnd) IO::store(pool + bs * slot_elems + head_off, part, t, hb);
     }
     }
 }
@@ -465,7 +455,7 @@ __global__ void __launch_bounds__(kThreads) accept_kernel(AcceptParams p)
     for (int i = 0; i < kPer; ++i) __builtin_nontemporal_store(x[i], o4 + threadIdx.x + kThreads * i);
 }
 
-template <typename StateT, bool ALIGN, int SPLIT, bool NT>
+template <typename StateT, bool ALIGN, int SPLIT>
 hipError_t launch_c(const CommitParams& p, hipStream_t s)
 {
     CommitParams args = p;
@@ -474,32 +464,27 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
     const uint64_t grid = (uint64_t)(args.ssm_wgs + p.conv_wgs);
     const void* fn =
         p.payload ? (p.conv_wgs > 0
-                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true, true>)
-                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false, true>))
+                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, true>)
+                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, true>))
                   : (p.conv_wgs > 0
-                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, true, false>)
-                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, NT, false, false>));
+                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, false>)
+                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false>));
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
 }
 
-template <bool ALIGN, int SPLIT, bool NT>
-hipError_t launch_c_dtype(const CommitParams& p, bool bf16_state, hipStream_t s)
-{
-    return bf16_state ? launch_c<uint16_t, ALIGN, SPLIT, NT>(p, s)
-                      : launch_c<float, ALIGN, SPLIT, NT>(p, s);
-}
-
+// Workgroups per head: the splits the launch chooses from (8 KiB per workgroup
+// for fp32 pools with up to 8 records and for bf16 pools, 32 KiB for fp32
+// pools with more records).
 template <bool ALIGN>
-hipError_t launch_c_shape(const CommitParams& p, bool bf16_state, int split, bool nt, hipStream_t s)
+hipError_t launch_c_split(const CommitParams& p, bool bf16_state, hipStream_t s)
 {
-    if (!nt) return hipErrorInvalidValue;   // cached state streams measured slower; not built
-    switch (split) {
-    case 1: return launch_c_dtype<ALIGN, 1, true>(p, bf16_state, s);
-    case 2: return launch_c_dtype<ALIGN, 2, true>(p, bf16_state, s);
-    case 4: return launch_c_dtype<ALIGN, 4, true>(p, bf16_state, s);
-    case 8: return launch_c_dtype<ALIGN, 8, true>(p, bf16_state, s);
-    default: return hipErrorInvalidValue;
+    if (bf16_state) {
+        static_assert(kCommitSplitBf16 == 4, "bf16 split");
+        return launch_c<uint16_t, ALIGN, kCommitSplitBf16>(p, s);
     }
+    static_assert(kCommitSplitF32 == 8 && kCommitSplitF32LongRecords == 2, "fp32 splits");
+    return p.T > 8 ? launch_c<float, ALIGN, kCommitSplitF32LongRecords>(p, s)
+                   : launch_c<float, ALIGN, kCommitSplitF32>(p, s);
 }
 
 template <typename StateT>
@@ -514,18 +499,9 @@ hipError_t launch_a(const AcceptParams& p, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool align, int split,
-                               bool nontemporal, hipStream_t s)
-{
-    return align ? launch_c_shape<true>(p, bf16_state, split, nontemporal, s)
-                 : launch_c_shape<false>(p, bf16_state, split, nontemporal, s);
-}
-
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s)
 {
-    const int split = bf16_state ? kCommitSplitBf16
-                                 : (p.T > 8 ? kCommitSplitF32LongRecords : kCommitSplitF32);
-    return launch_commit_shape(p, bf16_state, align, split, kCommitNontemporal, s);
+    return align ? launch_c_split<true>(p, bf16_state, s) : launch_c_split<false>(p, bf16_state, s);
 }
 
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s)

@@ -96,8 +96,10 @@ struct PlanParams {
 
 constexpr int kMaxRecTokens = GDN_MAX_REC_TOKENS;
 
-// Verify launch shape: rows of a head each thread holds (4, 2 or 1) and
-// threads per workgroup (256 or 512); a workgroup covers threads/8 * R rows.
+// Verify launch shape: rows of a head each thread holds and threads per
+// workgroup; a workgroup covers threads/8 * R rows (here 64: two workgroups
+// per head). One and four rows per thread and 512-thread workgroups measured
+// no faster.
 constexpr int kVerifyRowsPerThread = 2;
 constexpr int kVerifyThreads = 256;
 // Verify on fp32 pools with short windows (T <= 4) asks for at least this much
@@ -105,24 +107,20 @@ constexpr int kVerifyThreads = 256;
 // registers, which measured 2% faster (sweep of 0..34 KiB); bf16 pools run
 // best without a floor.
 constexpr int kVerifyLdsFloorF32 = 24 << 10;
-// Commit: workgroups per head (1, 2, 4 or 8) for fp32 and bf16 pools (8 KiB
-// per workgroup streams best for fp32 at up to 8 records, 32 KiB at more; 8
-// KiB for bf16); whether state loads and stores are nontemporal; whether
-// workgroup ids are remapped XCD-contiguous.
+// Commit: workgroups per head for fp32 and bf16 pools (8 KiB per workgroup
+// streams best for fp32 at up to 8 records, 32 KiB at more; 8 KiB for bf16;
+// one workgroup per head measured slower for both); whether workgroup ids are
+// remapped XCD-contiguous. State loads and stores are always nontemporal
+// (cached streams measured slower).
 constexpr int kCommitSplitF32 = 8;
 constexpr int kCommitSplitF32LongRecords = 2;   // fp32 pools with more than 8 records per row
 constexpr int kCommitSplitBf16 = 4;
-constexpr bool kCommitNontemporal = true;
 constexpr bool kCommitXcdRemap = true;
 
 // Launchers: return the hipError_t of the launch.
-hipError_t launch_verify_shape(const VerifyParams& p, bool bf16_state, bool snap, int R,
-                               int threads, hipStream_t s);
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hipStream_t s);
-hipError_t launch_commit_shape(const CommitParams& p, bool bf16_state, bool align, int split,
-                               bool nontemporal, hipStream_t s);
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_align_plan(const PlanParams& p, hipStream_t s);
 

@@ -474,50 +474,25 @@ hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
 }
 
 // The smallest compile-time window capacity that holds the record capacity.
-template <typename StateT, bool SNAP, int R, int NT>
+template <typename StateT, bool SNAP>
 hipError_t launch(const VerifyParams& p, hipStream_t s)
 {
+    constexpr int R = kVerifyRowsPerThread, NT = kVerifyThreads;
     if (p.T <= 4) return launch_tt<StateT, SNAP, R, NT, 4>(p, s);
     if (p.T <= 8) return launch_tt<StateT, SNAP, R, NT, 8>(p, s);
     return launch_tt<StateT, SNAP, R, NT, kMaxRecTokens>(p, s);
 }
 
-template <bool SNAP, int R, int NT>
-hipError_t launch_dtype(const VerifyParams& p, bool bf16_state, hipStream_t s)
-{
-    return bf16_state ? launch<uint16_t, SNAP, R, NT>(p, s) : launch<float, SNAP, R, NT>(p, s);
-}
-
-template <bool SNAP>
-hipError_t launch_shape(const VerifyParams& p, bool bf16_state, int R, int threads, hipStream_t s)
-{
-    switch (R * 1000 + threads) {
-    case 4256: return launch_dtype<SNAP, 4, 256>(p, bf16_state, s);
-    case 2256: return launch_dtype<SNAP, 2, 256>(p, bf16_state, s);
-    case 1256: return launch_dtype<SNAP, 1, 256>(p, bf16_state, s);
-    case 2512: return launch_dtype<SNAP, 2, 512>(p, bf16_state, s);
-    case 1512: return launch_dtype<SNAP, 1, 512>(p, bf16_state, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace
-
-hipError_t launch_verify_shape(const VerifyParams& p, bool bf16_state, bool snap, int R,
-                               int threads, hipStream_t s)
-{
-    return snap ? launch_shape<true>(p, bf16_state, R, threads, s)
-                : launch_shape<false>(p, bf16_state, R, threads, s);
-}
 
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return launch_verify_shape(p, bf16_state, false, kVerifyRowsPerThread, kVerifyThreads, s);
+    return bf16_state ? launch<uint16_t, false>(p, s) : launch<float, false>(p, s);
 }
 
 hipError_t launch_native_window(const VerifyParams& p, bool bf16_state, hipStream_t s)
 {
-    return launch_verify_shape(p, bf16_state, true, kVerifyRowsPerThread, kVerifyThreads, s);
+    return bf16_state ? launch<uint16_t, true>(p, s) : launch<float, true>(p, s);
 }
 
 }  // namespace gdn
