@@ -22,18 +22,21 @@
 // is the contraction of S0 with the 2w window vectors: 2w fmas per state
 // element instead of the per-token rule's 4w operations, and ring records cost
 // a scalar term each instead of a pass over the head. The 2w-column product is
-// a dense contraction; at w = 4 it fills half of an fp32 16x16x4 MFMA, and
-// matrix-core versions of this kernel measured no faster than this one (its
-// time is set by each workgroup's chain of memory latencies, not by the vector
-// ALU), so it stays on the vector ALU.
+// a dense contraction and its fmas are what separate this kernel from its
+// memory floor, but matrix-core versions measured slower (fp32 16x16x4 with half
+// of the columns idle at w = 4; 4x4x1 with none idle): the products then make a
+// round trip through LDS to a per-row recurrence, which costs more than the
+// vector fmas it saves. So the contraction stays on the vector ALU, fused with
+// the recurrence in registers.
 //
 // One workgroup of four wave64s per (row, value head, chunk of 32*R head rows);
 // workgroup ids are remapped so that each XCD streams a contiguous stretch of
-// the pool. Lane l holds head rows R*(l/8) + r and columns 4*(l%8) + 32*c + e
-// (c, e = 0..3): each 16-byte load of eight neighbouring lanes covers a whole
-// 128-byte row segment, and a length-128 reduction is 16 fmas in the lane plus
-// a three-step DPP sum over the eight lanes of a row group. The window's
-// vectors and the per-item scalar coefficients are staged in LDS once.
+// the pool. Thread t holds head rows row0 + R*(t/8) + r and columns
+// 4*(t%8) + 32*c + e (c, e = 0..3): each 16-byte load of eight neighbouring
+// lanes covers a whole 128-byte row segment, and a length-128 reduction is 16
+// fmas in the lane plus a three-step DPP sum over the eight lanes of a row
+// group. The window's vectors and the per-item scalar coefficients are staged
+// in LDS once.
 //
 // Options carried in the parameters: gates formed here from raw projections
 // (A_log, dt_bias), outputs rounded to bf16, and payload records (the raw key
