@@ -342,6 +342,19 @@ def main():
     log(f"step {wall:.3f} ms: verify graph {graph_ms:.3f} ms ({ver_ms * 1e3:.1f} us/layer), "
         f"commit {com_ms * 1e3:.1f} us")
 
+    # the same verify launches issued one by one, without the graph (outside the
+    # timed step): the host's launch cost per layer shows against the graph's
+    eager_steps = max(1, min(args.steps, 10))
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(eager_steps):
+        st.verify_all()
+    ev1.record()
+    torch.cuda.synchronize()
+    ver_eager_us = ev0.elapsed_time(ev1) * 1e3 / (eager_steps * launches)
+    assert st.err.item() == 0, f"device row errors {st.err.item()}"
+
     updates = acc["verify_updates"] + acc["commit_updates"]
     value = updates / (wall / 1e3)
     com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
@@ -380,6 +393,7 @@ def main():
         "roofline": roofline,
         "kernels": {
             "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": launches,
+                       "eager_us_per_launch": ver_eager_us,
                        "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
                        "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
             "commit_all_layers": {"us_per_launch": com_ms * 1e3, "launches_per_step": 1,

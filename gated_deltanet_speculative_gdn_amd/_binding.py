@@ -22,13 +22,13 @@ GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
 GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
 RECORD_CORRECTION, RECORD_PAYLOAD = 0, 1   # gdn_record_kind
 OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
-ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS = 1, 2, 4, 8, 16, 32, 64
+ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS, ROW_ALIAS = 1, 2, 4, 8, 16, 32, 64, 128
 PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2   # gdn_probe_kind
 GDN_PROBE_CHUNK = 16384
 
 EXPORTS = ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv", "gdn_align_plan",
            "gdn_native_window", "gdn_native_accept", "gdn_rec_stride", "gdn_record_stride",
-           "gdn_status_string", "gdn_abi_version", "gdn_bandwidth_probe")
+           "gdn_status_string", "gdn_abi_version", "gdn_bandwidth_probe", "gdn_check_slots")
 
 
 class GdnError(RuntimeError):
@@ -92,9 +92,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                                       vp, vp]
     lib.gdn_native_accept.argtypes = [P(gdn_pools), P(vp), i32, vp, vp, vp, vp]
     lib.gdn_bandwidth_probe.argtypes = [i32, vp, vp, i64, vp]
+    lib.gdn_check_slots.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp]
     for name in ("gdn_verify", "gdn_commit_all_layers", "gdn_commit_all_layers_conv",
                  "gdn_align_plan", "gdn_native_window", "gdn_native_accept", "gdn_abi_version",
-                 "gdn_bandwidth_probe"):
+                 "gdn_bandwidth_probe", "gdn_check_slots"):
         getattr(lib, name).restype = C.c_int32
     lib.gdn_rec_stride.argtypes = [i32]
     lib.gdn_rec_stride.restype = C.c_int64
@@ -333,3 +334,16 @@ def gdn_bandwidth_probe(kind: int, src, dst, nbytes: int | None = None, *, strea
         t = src if src is not None else dst
         nbytes = t.numel() * t.element_size()
     return _check(lib.gdn_bandwidth_probe(kind, _ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def gdn_check_slots(src_slot, dst_slot, n_accept, *, rec_slot=None, bnd_len=None, bnd_slot=None,
+                    err_flags, stream=None) -> int:
+    """Debug check of a commit's slot preconditions: ORs ROW_ALIAS into
+    ``err_flags`` if live rows share a written slot, write another row's
+    source or share a record slot."""
+    lib = load_library()
+    return _check(lib.gdn_check_slots(
+        src_slot.shape[0], _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
+        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
+        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
+        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))

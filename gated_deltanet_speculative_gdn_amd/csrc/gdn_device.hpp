@@ -22,7 +22,7 @@ constexpr float kSoftplusLinear = 20.f;  // softplus(x) = x above this input
 
 // Row-error bits, the values the C ABI documents.
 constexpr int kRowSlot = 1, kRowWin = 2, kRowN = 4, kRowBnd = 8, kRowTable = 16,
-              kRowRec = 32, kRowPos = 64;
+              kRowRec = 32, kRowPos = 64, kRowAlias = 128;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 #define GDN_MAX_LAYERS 64      /* layers per pool set */
 #define GDN_HEAD_DIM 128       /* K = V = 128 */
 #define GDN_MAX_REC_TOKENS 16  /* record capacity T per row */
@@ -82,7 +82,8 @@ enum {
                             or (plan) more than one block boundary inside the window */
     GDN_ROW_TABLE = 16,  /* (plan) block-table column out of range or empty where needed */
     GDN_ROW_REC = 32,    /* record slot < 0 or >= num_rec_slots for a live row */
-    GDN_ROW_POS = 64     /* (plan) num_computed < 1 */
+    GDN_ROW_POS = 64,    /* (plan) num_computed < 1 */
+    GDN_ROW_ALIAS = 128  /* (slot check) a slot shared between live rows; see gdn_check_slots */
 };
 
 /*
@@ -289,6 +290,34 @@ int32_t gdn_align_plan(int32_t num_rows, const int32_t* num_computed,
                        int32_t max_accept, int32_t* src_slot, int32_t* dst_slot,
                        int32_t* bnd_len, int32_t* bnd_slot, int32_t* err_flags,
                        void* stream);
+
+/*
+ * gdn_check_slots -- debug check of the slot preconditions that the hot-path
+ * calls state but do not check (the check is quadratic in the rows).
+ *
+ * The commit's rows run concurrently; the pages' align-mode race ([vLLM]
+ * Commits item 6) is one program overwriting a slot another still reads.
+ * Within a row the library is safe (every thread reads its source before it
+ * stores). Across rows, among the live rows (n_accept > 0 and src_slot >= 0),
+ * a row's written slots are its dst_slot and, when bnd_len > 0 and
+ * bnd_slot != dst_slot, its bnd_slot. For every live row that
+ *   - writes a slot another live row writes, or
+ *   - writes a slot another live row reads as its src_slot, or
+ *   - shares its rec_slot with another live row (when rec_slot is given),
+ * the kernel ORs GDN_ROW_ALIAS into *err_flags. It reads only the slot
+ * arrays and writes only *err_flags.
+ *
+ * src_slot, dst_slot, n_accept: device int32 [num_rows]; rec_slot: device
+ * int32 [num_rows] or NULL (not checked); bnd_len, bnd_slot: both device
+ * int32 [num_rows] or both NULL (no boundaries); err_flags: device int32
+ * (required). Host errors: num_rows < 0 (GDN_ERR_SHAPE), a missing required
+ * pointer or only one of bnd_len / bnd_slot (GDN_ERR_NULL). num_rows == 0
+ * returns GDN_OK without a launch.
+ */
+int32_t gdn_check_slots(int32_t num_rows, const int32_t* src_slot, const int32_t* dst_slot,
+                        const int32_t* rec_slot, const int32_t* n_accept,
+                        const int32_t* bnd_len, const int32_t* bnd_slot, int32_t* err_flags,
+                        void* stream);
 
 /*
  * gdn_native_window -- the baseline being replaced: the same verify

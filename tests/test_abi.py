@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.gdn_status_string(s), bytes)
     assert lib.gdn_status_string(-4).decode().startswith("a pointer or stride")
@@ -264,3 +264,14 @@ def test_bandwidth_probe_rejects_bad_arguments(lib):
     assert lib.gdn_bandwidth_probe(B.PROBE_WRITE, None, None, chunk, None) == E_NULL
     assert lib.gdn_bandwidth_probe(B.PROBE_COPY, odd, fake, chunk, None) == E_ALIGN
     assert lib.gdn_bandwidth_probe(B.PROBE_WRITE, None, odd, chunk, None) == E_ALIGN
+
+
+def test_check_slots_rejects_bad_arguments(lib):
+    fake = C.c_void_p(1 << 20)
+    assert lib.gdn_check_slots(-1, fake, fake, None, fake, None, None, fake, None) == E_SHAPE
+    assert lib.gdn_check_slots(4, None, fake, None, fake, None, None, fake, None) == E_NULL
+    assert lib.gdn_check_slots(4, fake, None, None, fake, None, None, fake, None) == E_NULL
+    assert lib.gdn_check_slots(4, fake, fake, None, None, None, None, fake, None) == E_NULL
+    assert lib.gdn_check_slots(4, fake, fake, None, fake, None, None, None, None) == E_NULL
+    assert lib.gdn_check_slots(4, fake, fake, None, fake, fake, None, fake, None) == E_NULL
+    assert lib.gdn_check_slots(0, fake, fake, None, fake, None, None, fake, None) == OK
