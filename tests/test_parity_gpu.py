@@ -205,8 +205,8 @@ def test_mtp_decode_b64_l48(gdn, dtype):
     assert h.err_value() == 0
 
 
-def ring_run(spec, sample_rows=None, check_all_untouched=True):
-    wl = W.make_workload(spec, device="cuda")
+def ring_run(spec, sample_rows=None, check_all_untouched=True, dtype=torch.float32):
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
     h = Harness(wl)
     pre = wl.state.clone()
     h.verify_all()                                   # 16 single-token steps per layer
@@ -258,6 +258,15 @@ def test_ring_align_b256_l36(gdn):
     assert (bl[r == 48] == 0).all() and (bl[r == 0] == 0).all()
     assert (bl[r == 49] == 15).all() and (bl[r == 63] == 1).all()
     assert (plan[3][bl > 0] == plan[0][bl > 0]).all(), "boundary state lands in the source slot"
+
+
+def test_ring_align_bf16_pool(gdn):
+    """The ring and its align-mode flush on a bf16 state pool: final and
+    boundary states equal RNE of the oracle's replay of the GPU records bit
+    for bit, and stay within one bf16 ulp of the fp32 native states."""
+    spec = W.shrink(W.RING_ALIGN, layers=2, rows=48, num_slots=112, hv=4, hk=2, seed=3100)
+    _, plan = ring_run(spec, dtype=torch.bfloat16)
+    assert (plan[2] > 0).any(), "no boundary in the sample"
 
 
 def test_align_boundary_in_source_slot_repeated(gdn):
