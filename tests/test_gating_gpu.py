@@ -120,3 +120,41 @@ def test_bf16_output_into_layer_view(gdn):
     ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1e-38))) - 7)
     slack = TOL * np.abs(ref).max()
     assert (np.abs(o - ref) <= ulp + slack).all(), "bf16 outputs: more than one ulp off"
+
+
+def test_raw_gates_with_payload_records(gdn):
+    """Raw-input gating and payload records together: the payload keeps the
+    decay and write strength formed in the kernel (bit-identical to the
+    correction record's decay from the same raw inputs), and the payload commit
+    lands within the fp32 tolerance of the oracle fed with its own gates."""
+    from test_payload_gpu import check_states, payload_fields
+    spec = W.shrink(W.ALL_LAYER, layers=2)
+    wl = W.make_workload(spec, device="cuda")
+    rg = W.make_raw_gates(wl, device="cuda")
+    hp = Harness(wl, record_kind=G.RECORD_PAYLOAD)
+    hc = Harness(wl)
+    pre = wl.state.clone()
+    for layer in range(spec.layers):
+        verify_raw(hp, rg, layer)
+        verify_raw(hc, rg, layer)
+    torch.cuda.synchronize()
+    assert torch.equal(hp.out.view(torch.int32), hc.out.view(torch.int32)), "outputs differ"
+    rows = np.arange(spec.rows)
+    og = oracle_gated(wl, rg)
+    for layer in range(spec.layers):
+        _, _, g, be = payload_fields(hp, layer, rows)
+        _, _, gc = hc.records(layer, rows)
+        assert_bitwise(g, gc, f"layer {layer} payload decays vs correction-record decays")
+        gd = OP.gather(og, layer, rows)
+        np.testing.assert_allclose(be, gd["beta"], rtol=1e-6, atol=0,
+                                   err_msg=f"layer {layer} payload write strengths")
+    hp.commit()
+    torch.cuda.synchronize()
+    assert hp.err_value() == 0
+    live = wl.n_accept > 0
+    for layer in range(spec.layers):
+        _, res = OP.run_layer(og, layer, rows, keep=wl.n_accept[:, None], state=pre[layer])
+        slots = torch.as_tensor(wl.state_slot[live].astype(np.int64), device="cuda")
+        got = wl.state[layer].index_select(0, slots).reshape(-1, 128, 128)
+        check_states(got, res.kept[np.repeat(live, spec.hv), 0], torch.float32,
+                     f"layer {layer} payload-commit states with raw gates")
