@@ -11,6 +11,9 @@ shared library and marshals numpy arrays:
 * :func:`native_heads` -- the native per-token gated delta rule over packed,
   independent heads (the plain definition: every state kept).
 * :func:`replay_heads` -- replay of recorded tokens (the commit update).
+* :func:`native_heads_ch`, :func:`replay_heads_ch` -- the same with one decay
+  per key channel (the KDA reading: the pages name Kimi-K3 KDA as a user of
+  the same protocol but print none of its arithmetic).
 * :func:`align_plan` -- align-mode source / final / boundary slots, by walking
   token positions.
 * :func:`bf16_to_f32`, :func:`f32_to_bf16_rne` -- exact widening and
@@ -75,6 +78,15 @@ def _load():
             fn.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int,
                            rp, i32p, rp, rp, rp, rp, rp, rc, rc,
                            rp, rp, rp, rp, vp, vp, vp, C.c_int, C.c_int]
+        for suf, rp, rc in (("f32", f32p, C.c_float), ("f64", f64p, C.c_double)):
+            fn = getattr(lib, f"gdno_native_heads_ch_{suf}")
+            fn.restype = C.c_int
+            fn.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int,
+                           rp, i32p, rp, rp, rp, rp, rp, rc, rc,
+                           rp, rp, rp, rp, vp, vp, vp, C.c_int, C.c_int]
+        lib.gdno_replay_heads_ch_f32.restype = C.c_int
+        lib.gdno_replay_heads_ch_f32.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, f32p, i32p,
+                                                 f32p, f32p, f32p, C.c_int]
         for suf, rp in (("f32", f32p), ("f64", f64p)):
             fn = getattr(lib, f"gdno_raw_gates_{suf}")
             fn.restype = C.c_int
@@ -114,6 +126,7 @@ class NativeResult:
     rec_g: np.ndarray      # [H][T]
     snaps: np.ndarray | None  # [H][T][V][K]: S_1..S_T (only the first w per head valid)
     kept: np.ndarray | None   # [H][nkeep][V][K]
+    rec_alpha: np.ndarray | None = None  # [H][T][K] per-channel decays (channel variant)
 
 
 def _c(x, dt):
@@ -158,6 +171,56 @@ def native_heads(S0, w, q, k, v, a, beta, *, scale=1.0, eps=EPS, snaps=False,
     if rc != 0:
         raise ValueError("oracle native_heads rejected its arguments")
     return NativeResult(o, rd, rk, rg, sn, kept)
+
+
+def native_heads_ch(S0, w, q, k, v, a, beta, *, scale=1.0, eps=EPS, snaps=False,
+                    keep=None, dtype=np.float32, nthreads=None) -> NativeResult:
+    """The per-key-channel decay variant of :func:`native_heads`: a [H][T][K]
+    holds one log-decay per key channel. ``rec_g`` of the result is None and
+    ``rec_alpha`` [H][T][K] holds the decays."""
+    lib = _load()
+    S0 = _c(S0, dtype)
+    H, V, K = S0.shape
+    q = _c(q, dtype)
+    T = q.shape[1]
+    k, v, a, beta = _c(k, dtype), _c(v, dtype), _c(a, dtype), _c(beta, dtype)
+    w = _c(w, np.int32)
+    assert q.shape == (H, T, K) and k.shape == (H, T, K) and v.shape == (H, T, V)
+    assert a.shape == (H, T, K) and beta.shape == (H, T) and w.shape == (H,)
+    o = np.zeros((H, T, V), dtype)
+    rd = np.zeros((H, T, V), dtype)
+    rk = np.zeros((H, T, K), dtype)
+    ra = np.zeros((H, T, K), dtype)
+    sn = np.zeros((H, T, V, K), dtype) if snaps else None
+    nkeep, kept, keep_arr = 0, None, None
+    if keep is not None:
+        keep_arr = _c(keep, np.int32).reshape(H, -1)
+        nkeep = keep_arr.shape[1]
+        kept = np.zeros((H, nkeep, V, K), dtype)
+    fn = lib.gdno_native_heads_ch_f32 if dtype == np.float32 else lib.gdno_native_heads_ch_f64
+    rc = fn(H, K, V, T, S0, w, q, k, v, a, beta, scale, eps, o, rd, rk, ra,
+            sn.ctypes.data if sn is not None else None,
+            keep_arr.ctypes.data if keep_arr is not None else None,
+            kept.ctypes.data if kept is not None else None,
+            nkeep, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle native_heads_ch rejected its arguments")
+    return NativeResult(o, rd, rk, None, sn, kept, ra)
+
+
+def replay_heads_ch(S, n, rec_delta, rec_khat, rec_alpha, *, nthreads=None) -> np.ndarray:
+    """Return a copy of S [H][V][K] with n[h] per-channel-decay records replayed."""
+    lib = _load()
+    S = np.array(S, dtype=np.float32, order="C", copy=True)
+    H, V, K = S.shape
+    rd, rk, ra = _c(rec_delta, np.float32), _c(rec_khat, np.float32), _c(rec_alpha, np.float32)
+    T = rd.shape[1]
+    assert rd.shape == (H, T, V) and rk.shape == (H, T, K) and ra.shape == (H, T, K)
+    rc = lib.gdno_replay_heads_ch_f32(H, K, V, T, S, _c(n, np.int32), rd, rk, ra,
+                                      nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle replay_heads_ch rejected its arguments")
+    return S
 
 
 def replay_heads(S, n, rec_delta, rec_khat, rec_g, *, nthreads=None) -> np.ndarray:

@@ -132,6 +132,80 @@ int gdno_native_heads_##SUF(int nheads, int K, int V, int T,                    
 BATCH_NATIVE(f32, float)
 BATCH_NATIVE(f64, double)
 
+/* The per-key-channel decay variant, batched like gdno_native_heads: a and
+ * rec_alpha are [nheads][T][K] (a log-decay and a decay per key channel);
+ * everything else as there. */
+#define BATCH_NATIVE_CH(SUF, R)                                                         \
+int gdno_native_heads_ch_##SUF(int nheads, int K, int V, int T,                         \
+    const R* S0, const int* w, const R* q, const R* k, const R* v,                      \
+    const R* a, const R* beta, R scale, R eps,                                          \
+    R* o, R* rec_delta, R* rec_khat, R* rec_alpha, R* snaps,                            \
+    const int* keep, R* kept, int nkeep, int nthreads)                                  \
+{                                                                                       \
+    if (nheads < 0 || K < 1 || V < 1 || T < 1 || nkeep < 0) return -1;                  \
+    for (int i = 0; i < nheads; ++i) if (w[i] < 0 || w[i] > T) return -1;               \
+    if (keep)                                                                           \
+        for (long i = 0; i < (long)nheads * nkeep; ++i)                                 \
+            if (keep[i] > w[i / (nkeep ? nkeep : 1)]) return -1;                        \
+    const long VK = (long)V * K;                                                        \
+    int bad = 0;                                                                        \
+    _Pragma("omp parallel num_threads(nthreads > 0 ? nthreads : 1)")                    \
+    {                                                                                   \
+        R* h = (R*)malloc(sizeof(R) * VK);                                              \
+        R* qt = (R*)malloc(sizeof(R) * K);                                              \
+        R* kh = (R*)malloc(sizeof(R) * K);                                              \
+        R* al = (R*)malloc(sizeof(R) * K);                                              \
+        R* loc = (R*)malloc(sizeof(R) * VK * (T + 1));                                  \
+        int ok = h && qt && kh && al && loc;                                            \
+        if (!ok) {                                                                      \
+            _Pragma("omp atomic write") bad = 1;                                        \
+        }                                                                               \
+        {                                                                               \
+            _Pragma("omp for schedule(dynamic, 4)")                                     \
+            for (int i = 0; i < nheads; ++i) {                                          \
+                if (!ok) continue;                                                      \
+                const long tk = (long)i * T;                                            \
+                memcpy(loc, S0 + i * VK, sizeof(R) * VK);                               \
+                native_head_ch_##SUF(K, V, S0 + i * VK, w[i], q + tk * K, k + tk * K,   \
+                    v + tk * V, a + tk * K, beta + tk, scale, eps, h, qt, kh, al,       \
+                    o + tk * V, rec_delta + tk * V, rec_khat + tk * K,                  \
+                    rec_alpha + tk * K, loc + VK);                                      \
+                if (snaps)                                                              \
+                    memcpy(snaps + tk * VK, loc + VK, sizeof(R) * VK * w[i]);           \
+                if (keep)                                                               \
+                    for (int j = 0; j < nkeep; ++j) {                                   \
+                        int s = keep[(long)i * nkeep + j];                              \
+                        if (s >= 0)                                                     \
+                            memcpy(kept + ((long)i * nkeep + j) * VK, loc + s * VK,     \
+                                   sizeof(R) * VK);                                     \
+                    }                                                                   \
+            }                                                                           \
+        }                                                                               \
+        free(h); free(qt); free(kh); free(al); free(loc);                               \
+    }                                                                                   \
+    return bad ? -1 : 0;                                                                \
+}
+
+BATCH_NATIVE_CH(f32, float)
+BATCH_NATIVE_CH(f64, double)
+
+/* Replay n[i] per-channel-decay records of head i onto S[i] in place. */
+int gdno_replay_heads_ch_f32(int nheads, int K, int V, int T, float* S, const int* n,
+                             const float* rec_delta, const float* rec_khat,
+                             const float* rec_alpha, int nthreads)
+{
+    if (nheads < 0 || K < 1 || V < 1 || T < 1) return -1;
+    for (int i = 0; i < nheads; ++i) if (n[i] < 0 || n[i] > T) return -1;
+    const long VK = (long)V * K;
+    #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int i = 0; i < nheads; ++i) {
+        const long tk = (long)i * T;
+        replay_head_ch_f32(K, V, S + i * VK, n[i], rec_delta + tk * V, rec_khat + tk * K,
+                           rec_alpha + tk * K);
+    }
+    return 0;
+}
+
 /* Gates from raw inputs for n (token, value head) entries laid out
  * [tokens][HV] (head fastest): entry i uses A_log[i % hv], dt_bias[i % hv].
  * Writes the log-gate (the decay is exp of it) and beta. Return 0, or -1 on

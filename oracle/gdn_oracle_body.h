@@ -111,6 +111,72 @@ static void GLUE(replay_head_, SUFFIX)(
 }
 
 
+/*
+ * The per-key-channel decay variant (the KDA reading: the pages name Kimi-K3
+ * KDA as a user of the same record-and-replay protocol but give none of its
+ * arithmetic; the reading taken is the gated delta rule with the scalar decay
+ * replaced by one decay per key channel). For token t the log-decay is a
+ * K-vector a_t and alpha_t[k] = exp(a_t[k]); then
+ *   h'[v][k] = h[v][k] * alpha_t[k]      (rounded; the value replay uses)
+ *   u, delta, the update and o as in native_head above,
+ * and the record is (delta[t], k_hat[t], alpha_t). With alpha_t[k] equal for
+ * every k this is native_head exactly. al is a K-element work array.
+ */
+static void GLUE(native_head_ch_, SUFFIX)(
+    int K, int V, const REAL* S0, int w,
+    const REAL* q, const REAL* k, const REAL* vv, const REAL* a, const REAL* beta,
+    REAL scale, REAL eps,
+    REAL* h, REAL* qt, REAL* kh, REAL* al,
+    REAL* o, REAL* rec_delta, REAL* rec_khat, REAL* rec_alpha, REAL* snaps)
+{
+    for (long e = 0; e < (long)V * K; ++e) h[e] = S0[e];
+    for (int t = 0; t < w; ++t) {
+        const REAL* qv = q + (long)t * K;
+        const REAL* kv = k + (long)t * K;
+        const REAL* vt = vv + (long)t * V;
+        GLUE(l2norm_, SUFFIX)(K, qv, eps, scale, qt);
+        GLUE(l2norm_, SUFFIX)(K, kv, eps, (REAL)1, kh);
+        for (int kk = 0; kk < K; ++kk) al[kk] = EXP(a[(long)t * K + kk]);
+        REAL b = beta[t];
+        for (int v = 0; v < V; ++v) {
+            REAL* hr = h + (long)v * K;
+            for (int kk = 0; kk < K; ++kk) hr[kk] = hr[kk] * al[kk];
+            REAL u = 0;
+            for (int kk = 0; kk < K; ++kk) u = u + hr[kk] * kh[kk];
+            REAL d = b * (vt[v] - u);
+            for (int kk = 0; kk < K; ++kk) hr[kk] = FMA(d, kh[kk], hr[kk]);
+            REAL ov = 0;
+            for (int kk = 0; kk < K; ++kk) ov = ov + hr[kk] * qt[kk];
+            o[(long)t * V + v] = ov;
+            rec_delta[(long)t * V + v] = d;
+        }
+        for (int kk = 0; kk < K; ++kk) {
+            rec_khat[(long)t * K + kk] = kh[kk];
+            rec_alpha[(long)t * K + kk] = al[kk];
+        }
+        if (snaps)
+            for (long e = 0; e < (long)V * K; ++e) snaps[(long)t * V * K + e] = h[e];
+    }
+}
+
+/* Replay of n per-channel-decay records:
+ * h[v][k] = fma(delta_t[v], k_hat_t[k], h[v][k] * alpha_t[k]), t = 0..n-1. */
+static void GLUE(replay_head_ch_, SUFFIX)(
+    int K, int V, REAL* h, int n,
+    const REAL* rec_delta, const REAL* rec_khat, const REAL* rec_alpha)
+{
+    for (int t = 0; t < n; ++t) {
+        const REAL* d = rec_delta + (long)t * V;
+        const REAL* kh = rec_khat + (long)t * K;
+        const REAL* al = rec_alpha + (long)t * K;
+        for (int v = 0; v < V; ++v)
+            for (int kk = 0; kk < K; ++kk) {
+                REAL decayed = h[(long)v * K + kk] * al[kk];
+                h[(long)v * K + kk] = FMA(d[v], kh[kk], decayed);
+            }
+    }
+}
+
 /* Gates from the raw per-token projections a, b of one value head with that
  * head's parameters A_log, dt_bias. The pages give no formula for this step;
  * the reading taken is the decay parameterisation used with Gated DeltaNet

@@ -5,7 +5,10 @@ invariants of the method, closed forms of the gated delta rule, the
 transition-matrix form of the rule evaluated in fp64, one-hot inputs whose
 reductions have a single term, the page's record-size figure, hand-worked
 align plans, an independent closed form of the align plan, and torch's bf16
-rounding. A dropped term, a wrong sign, a transposed operand or a wrong index
+rounding. The per-key-channel decay variant (the KDA reading) is pinned to the
+scalar rule (a decay repeated over the channels gives it bit for bit), to its
+own replay, to the per-column closed form at beta = 0 and to its fp64
+transition-matrix form. A dropped term, a wrong sign, a transposed operand or a wrong index
 in the oracle fails at least one of them.
 """
 import json
@@ -453,3 +456,108 @@ def test_conv_decode_is_a_sliding_window(Ls):
     a = 4
     mid = oracle.conv_decode(state, x[:a])[a]
     np.testing.assert_array_equal(oracle.conv_decode(mid, x[a:])[-1], walk[-1])
+
+
+# --------------------------------------------------------------------------
+# The per-key-channel decay variant (the KDA reading)
+# --------------------------------------------------------------------------
+
+def _channel_a(seed, H, T, K, extreme=False):
+    rng = np.random.default_rng(1000 + seed)
+    a = (-np.logaddexp(0, rng.normal(size=(H, T, K)))).astype(F32)
+    if extreme:
+        a[:, 0, : K // 2] = 0.0      # no decay on half of the channels
+        a[:, 1, K // 2:] = -100.0    # decay to the subnormal range on the others
+    return a
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("extreme", [False, True])
+def test_channel_uniform_decay_is_the_scalar_rule(seed, extreme):
+    """One decay repeated over every key channel gives the scalar rule's
+    outputs, records and states bit for bit (fp32 and fp64)."""
+    S0, q, k, v, a, beta = _inputs(seed, K=32, V=24, extreme=extreme)
+    w = np.array([4, 3, 1], np.int32)
+    ach = np.repeat(a[:, :, None], 32, 2)
+    for dt in (np.float32, np.float64):
+        r = oracle.native_heads(S0, w, q, k, v, a, beta, snaps=True, dtype=dt)
+        c = oracle.native_heads_ch(S0, w, q, k, v, ach, beta, snaps=True, dtype=dt)
+        for x, y in ((r.o, c.o), (r.rec_delta, c.rec_delta), (r.rec_khat, c.rec_khat),
+                     (r.snaps, c.snaps), (np.repeat(r.rec_g[:, :, None], 32, 2), c.rec_alpha)):
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("K,V,T", [(4, 4, 4), (16, 12, 5), (128, 128, 4)])
+def test_channel_replay_equals_native_state(seed, K, V, T):
+    S0, q, k, v, _, beta = _inputs(seed, H=2, T=T, K=K, V=V)
+    a = _channel_a(seed, 2, T, K)
+    w = np.array([T, T - 2], np.int32)
+    r = oracle.native_heads_ch(S0, w, q, k, v, a, beta, snaps=True)
+    for h in range(2):
+        for n in range(w[h] + 1):
+            got = oracle.replay_heads_ch(S0[h:h + 1], [n], r.rec_delta[h:h + 1],
+                                         r.rec_khat[h:h + 1], r.rec_alpha[h:h + 1])[0]
+            want = S0[h] if n == 0 else r.snaps[h, n - 1]
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (h, n)
+
+
+def test_channel_no_write_decays_each_key_column():
+    """beta = 0: S_t[v][k] = S_{t-1}[v][k] * alpha_t[k] exactly (columns are the
+    key channels; a state scaled along its value rows instead fails)."""
+    S0, q, k, v, _, beta = _inputs(5, K=16, V=16)
+    a = _channel_a(5, 3, 4, 16)
+    beta[:] = 0
+    r = oracle.native_heads_ch(S0, np.full(3, 4, np.int32), q, k, v, a, beta, snaps=True)
+    S = S0.copy()
+    for t in range(4):
+        al = r.rec_alpha[:, t]
+        S = (S * al[:, None, :]).astype(F32)
+        assert np.array_equal(r.snaps[:, t], S)
+    rows_scaled = (S0 * r.rec_alpha[:, 0][:, :, None]).astype(F32)
+    assert not np.array_equal(r.snaps[:, 0], rows_scaled)
+    assert np.array_equal(r.rec_delta, np.zeros_like(r.rec_delta))
+
+
+def _channel_transition_form(S0, q, k, v, a, beta, scale):
+    """S_t = S_{t-1} Diag(alpha_t) (I - beta k k^T) + beta v k^T in fp64."""
+    H, T, K = q.shape
+    S = S0.astype(np.float64)
+    outs, states = [], []
+    eye = np.eye(K)
+    for t in range(T):
+        kh = _norm64(k[:, t])
+        qh = _norm64(q[:, t]) * scale
+        al = np.exp(a[:, t].astype(np.float64))
+        b = beta[:, t].astype(np.float64)
+        P = eye[None] - b[:, None, None] * kh[:, :, None] * kh[:, None, :]
+        S = (S * al[:, None, :]) @ P + b[:, None, None] * v[:, t].astype(np.float64)[:, :, None] * kh[:, None, :]
+        outs.append(np.einsum("hvk,hk->hv", S, qh))
+        states.append(S.copy())
+    return np.stack(outs, 1), np.stack(states, 1)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("extreme", [False, True])
+def test_channel_matches_transition_matrix_form(seed, extreme):
+    S0, q, k, v, _, beta = _inputs(seed, K=128, V=128)
+    a = _channel_a(seed, 3, 4, 128, extreme=extreme)
+    o64, s64 = _channel_transition_form(S0, q, k, v, a, beta, 1.0)
+    w = np.full(3, 4, np.int32)
+    r32 = oracle.native_heads_ch(S0, w, q, k, v, a, beta, snaps=True)
+    r64 = oracle.native_heads_ch(S0, w, q, k, v, a, beta, snaps=True, dtype=np.float64,
+                                 eps=float(F32(oracle.EPS)))
+    for t in range(4):
+        assert _relerr(r32.o[:, t], o64[:, t]) < 1e-5
+        assert _relerr(r32.snaps[:, t], s64[:, t]) < 1e-5
+        assert _relerr(r64.o[:, t], o64[:, t]) < 1e-11
+        assert _relerr(r64.snaps[:, t], s64[:, t]) < 1e-11
+
+
+def test_channel_record_decay_is_exp():
+    S0, q, k, v, _, beta = _inputs(12, K=128, V=128)
+    a = _channel_a(12, 3, 4, 128)
+    r = oracle.native_heads_ch(S0, np.full(3, 4, np.int32), q, k, v, a, beta)
+    al64 = np.exp(a.astype(np.float64))
+    assert np.all(np.abs(r.rec_alpha - al64) <= np.spacing(r.rec_alpha.astype(F32)))
+    assert r.rec_g is None
