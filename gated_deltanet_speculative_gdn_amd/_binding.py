@@ -19,8 +19,8 @@ GDN_MAX_LAYERS = 64
 GDN_HEAD_DIM = 128
 GDN_MAX_REC_TOKENS = 16
 GDN_STATE_F32, GDN_STATE_BF16 = 0, 1
-GATE_LOG, GATE_RAW = 0, 1            # gdn_gate_mode
-RECORD_CORRECTION, RECORD_PAYLOAD = 0, 1   # gdn_record_kind
+GATE_LOG, GATE_RAW, GATE_CHANNEL = 0, 1, 2          # gdn_gate_mode
+RECORD_CORRECTION, RECORD_PAYLOAD, RECORD_CHANNEL = 0, 1, 2   # gdn_record_kind
 OUT_F32, OUT_BF16 = 0, 1             # gdn_out_dtype
 ROW_SLOT, ROW_WIN, ROW_N, ROW_BND, ROW_TABLE, ROW_REC, ROW_POS, ROW_ALIAS = 1, 2, 4, 8, 16, 32, 64, 128
 PROBE_READ, PROBE_WRITE, PROBE_COPY = 0, 1, 2   # gdn_probe_kind
@@ -66,6 +66,7 @@ class gdn_verify_io(C.Structure):
         ("num_tokens", C.c_int64), ("scale", C.c_float), ("gate_mode", C.c_int32),
         ("A_log", C.c_void_p), ("dt_bias", C.c_void_p),
         ("out_dtype", C.c_int32), ("reserved", C.c_int32),
+        ("decay_tok_stride", C.c_int64),
     ]
 
 
@@ -215,10 +216,18 @@ class ConvPools:
 
 
 def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
+    """a [tokens][HV] (log-gate, or raw projection with A_log / dt_bias) or
+    a [tokens][HV][128] (one log-decay per key channel); b [tokens][HV]."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
             raise TypeError(f"{name} must be a bf16 [tokens][heads][128] view, feature-contiguous")
-    if a.dtype != torch.float32 or b.dtype != torch.float32 or a.dim() != 2 \
+    channel = a.dim() == 3
+    if channel:
+        if a.dtype != torch.float32 or a.stride(2) != 1 or a.stride(1) != a.shape[2] \
+                or b.dtype != torch.float32 or b.dim() != 2 or b.stride(1) != 1:
+            raise TypeError("per-channel decays: a fp32 [tokens][HV][128] (heads packed), "
+                            "b fp32 [tokens][HV]")
+    elif a.dtype != torch.float32 or b.dtype != torch.float32 or a.dim() != 2 \
             or a.stride(1) != 1 or b.stride() != a.stride():
         raise TypeError("a and b must be fp32 [tokens][HV] with the same strides")
     if out.dtype not in (torch.float32, torch.bfloat16) or out.dim() != 3 or out.stride(2) != 1:
@@ -229,12 +238,17 @@ def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     io.q, io.q_tok_stride, io.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
     io.k, io.k_tok_stride, io.k_head_stride = k.data_ptr(), k.stride(0), k.stride(1)
     io.v, io.v_tok_stride, io.v_head_stride = v.data_ptr(), v.stride(0), v.stride(1)
-    io.a, io.b, io.gate_tok_stride = a.data_ptr(), b.data_ptr(), a.stride(0)
+    io.a, io.b, io.gate_tok_stride = a.data_ptr(), b.data_ptr(), b.stride(0)
     io.out, io.out_tok_stride, io.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
     io.out_dtype = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a.shape[0], out.shape[0])
     io.scale = float(scale)
     io.gate_mode = GATE_LOG
+    if channel:
+        if A_log is not None:
+            raise TypeError("per-channel decays are given as log-decays, not raw projections")
+        io.gate_mode = GATE_CHANNEL
+        io.decay_tok_stride = a.stride(0)
     if A_log is not None:
         for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
             if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():

@@ -27,7 +27,8 @@ int32_t check_pools(const gdn_pools* p)
     if (p->state_dtype != GDN_STATE_F32 && p->state_dtype != GDN_STATE_BF16) return GDN_ERR_DTYPE;
     if (p->num_state_slots < 1 || p->num_rec_slots < 1) return GDN_ERR_SHAPE;
     if (p->rec_tokens < 1 || p->rec_tokens > GDN_MAX_REC_TOKENS) return GDN_ERR_SHAPE;
-    if (p->record_kind != GDN_RECORD_CORRECTION && p->record_kind != GDN_RECORD_PAYLOAD)
+    if (p->record_kind != GDN_RECORD_CORRECTION && p->record_kind != GDN_RECORD_PAYLOAD &&
+        p->record_kind != GDN_RECORD_CHANNEL)
         return GDN_ERR_SHAPE;
     return GDN_OK;
 }
@@ -44,7 +45,9 @@ int32_t check_io(const gdn_verify_io* io)
 {
     if (!io) return GDN_ERR_NULL;
     if (!io->q || !io->k || !io->v || !io->a || !io->b || !io->out) return GDN_ERR_NULL;
-    if (io->gate_mode != GDN_GATE_LOG && io->gate_mode != GDN_GATE_RAW) return GDN_ERR_SHAPE;
+    if (io->gate_mode != GDN_GATE_LOG && io->gate_mode != GDN_GATE_RAW &&
+        io->gate_mode != GDN_GATE_CHANNEL)
+        return GDN_ERR_SHAPE;
     if (io->out_dtype != GDN_OUT_F32 && io->out_dtype != GDN_OUT_BF16) return GDN_ERR_DTYPE;
     if (io->gate_mode == GDN_GATE_RAW && (!io->A_log || !io->dt_bias)) return GDN_ERR_NULL;
     if (io->num_tokens < 0 || io->gate_tok_stride < 0) return GDN_ERR_SHAPE;
@@ -64,6 +67,10 @@ int32_t check_io(const gdn_verify_io* io)
     if (((uintptr_t)io->a & 3u) || ((uintptr_t)io->b & 3u)) return GDN_ERR_ALIGN;
     if (io->gate_mode == GDN_GATE_RAW && (((uintptr_t)io->A_log & 3u) || ((uintptr_t)io->dt_bias & 3u)))
         return GDN_ERR_ALIGN;
+    if (io->gate_mode == GDN_GATE_CHANNEL) {
+        if (io->decay_tok_stride < 0) return GDN_ERR_SHAPE;
+        if (!aligned16(io->a) || (io->decay_tok_stride & 3)) return GDN_ERR_ALIGN;
+    }
     return GDN_OK;
 }
 
@@ -97,6 +104,8 @@ void fill_io(VerifyParams& v, const gdn_verify_io* io)
     v.A_log = io->A_log; v.dt_bias = io->dt_bias;
     v.out = io->out; v.o_ts = io->out_tok_stride; v.o_hs = io->out_head_stride;
     v.out_bf16 = io->out_dtype == GDN_OUT_BF16;
+    v.channel = io->gate_mode == GDN_GATE_CHANNEL;
+    v.a_ts = io->decay_tok_stride;
     v.num_tokens = io->num_tokens;
     v.scale = io->scale;
 }
@@ -117,6 +126,7 @@ int64_t gdn_record_stride(int32_t rec_tokens, int32_t record_kind)
 {
     if (rec_tokens < 1) return 0;
     if (record_kind == GDN_RECORD_CORRECTION) return gdn_rec_stride(rec_tokens);
+    if (record_kind == GDN_RECORD_CHANNEL) return (int64_t)rec_tokens * 3 * GDN_HEAD_DIM;
     if (record_kind != GDN_RECORD_PAYLOAD) return 0;
     const int64_t bytes = (int64_t)rec_tokens * (2 * GDN_HEAD_DIM * 2 + 8);
     return ((bytes + 15) & ~(int64_t)15) / 4;
@@ -151,6 +161,11 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     if ((st = check_io(io))) return st;
     if (!state_slot || !rec_slot || !tok_start || !win_len) return GDN_ERR_NULL;
     if (rec_base && pools->record_kind == GDN_RECORD_PAYLOAD) return GDN_ERR_SHAPE;
+    if ((pools->record_kind == GDN_RECORD_CHANNEL) != (io->gate_mode == GDN_GATE_CHANNEL))
+        return GDN_ERR_SHAPE;
+    if (io->gate_mode == GDN_GATE_CHANNEL &&
+        io->decay_tok_stride < (int64_t)pools->num_v_heads * GDN_HEAD_DIM)
+        return GDN_ERR_SHAPE;
     if (num_rows == 0) return GDN_OK;
 
     VerifyParams v;
@@ -189,6 +204,9 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
     if ((st = check_io(io))) return st;
     if (!state_slot || !tok_start || !win_len || !snap) return GDN_ERR_NULL;
     if (!aligned16(snap)) return GDN_ERR_ALIGN;
+    if (io->gate_mode == GDN_GATE_CHANNEL &&
+        io->decay_tok_stride < (int64_t)pools->num_v_heads * GDN_HEAD_DIM)
+        return GDN_ERR_SHAPE;
     if (num_rows == 0) return GDN_OK;
 
     VerifyParams v;
@@ -263,6 +281,7 @@ int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools*
         c.rec_slot = rec_slot;
         c.rec_stride = gdn_record_stride(pools->rec_tokens, pools->record_kind);
         c.payload = pools->record_kind == GDN_RECORD_PAYLOAD;
+        c.channel = pools->record_kind == GDN_RECORD_CHANNEL;
         c.hv = pools->num_v_heads;
         c.num_slots = pools->num_state_slots;
         c.num_rec_slots = pools->num_rec_slots;

@@ -166,7 +166,7 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
     }
 }
 
-template <typename StateT, bool ALIGN, int SPLIT, bool CONV, bool PAY>
+template <typename StateT, bool ALIGN, int SPLIT, bool CONV, bool PAY, bool CH>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
     if constexpr (CONV) {
@@ -181,7 +181,8 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     const int T = p.T;
     float* d_l = lds;                 // [n][kRows] corrections (payload: values) of the owned rows
     float* k_l = lds + T * kDim;      // [n][128] normalised keys
-    float* g_l = lds + 2 * T * kDim;  // [n] decays (payload: then [n] write strengths)
+    float* g_l = lds + 2 * T * kDim;  // [n] decays (payload: then [n] write strengths;
+                                      // per-channel records: [n][128] decays)
 
     // logical id: (layer, row, value head, part), XCD-contiguous
     const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, p.ssm_wgs) : blockIdx.x;
@@ -225,7 +226,7 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     // a decay and a write strength.
     constexpr int kDChunks = (kMaxRecTokens * kRow4 + kThreads - 1) / kThreads;
     constexpr int kKChunks = (kMaxRecTokens * (kDim / 4) + kThreads - 1) / kThreads;
-    f32x4 rd[kDChunks], rk[kKChunks];
+    f32x4 rd[kDChunks], rk[kKChunks], ra[CH ? kKChunks : 1];
     float rg = 0.f, rb = 0.f;
     u32x4 pk = {0u, 0u, 0u, 0u};
     u32x2 pv[kDChunks];
@@ -259,6 +260,13 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         for (int q = 0; q < kKChunks; ++q) {
             const int i = t + q * kThreads;
             if (i < n * (kDim / 4)) rk[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
+        }
+        if constexpr (CH) {   // per-channel decays, laid out like the keys
+#pragma unroll
+            for (int q = 0; q < kKChunks; ++q) {
+                const int i = t + q * kThreads;
+                if (i < n * (kDim / 4)) ra[q] = ld4(recb + 2 * (int64_t)T * kDim + 4 * i);
+            }
         }
         if (t < n) rg = recb[2 * (int64_t)T * kDim + t];
     }
@@ -369,7 +377,15 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         const int i = t + q * kThreads;
         if (i < n * (kDim / 4)) st4(k_l + 4 * i, rk[q]);
     }
-    if (t < n) g_l[t] = rg;
+    if constexpr (CH) {
+#pragma unroll
+        for (int q = 0; q < kKChunks; ++q) {
+            const int i = t + q * kThreads;
+            if (i < n * (kDim / 4)) st4(g_l + 4 * i, ra[q]);
+        }
+    } else {
+        if (t < n) g_l[t] = rg;
+    }
     __syncthreads();
 
     // ---- replay piece by piece, h = fma(delta_t[row], k_hat_t[col], h * g_t)
@@ -381,11 +397,17 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         for (int i = 0; i < IO::kPer; ++i) {
             const int row = IO::local_row(t, i);
             for (int tt = 0; tt < n; ++tt) {
-                const float g = g_l[tt];
                 const f32x4 kh = ld4(k_l + tt * kDim + c0);
                 const float d = d_l[tt * kRows + row];
+                if constexpr (CH) {          // per-channel decay, column by column
+                    const f32x4 al = ld4(g_l + tt * kDim + c0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * g);
+                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * al[e]);
+                } else {
+                    const float g = g_l[tt];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * g);
+                }
                 if constexpr (ALIGN) {
                     if (tt + 1 == bl) hb[i] = h[i];
                 }
@@ -396,14 +418,24 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
         for (int i = 0; i < IO::kPer / 2; ++i) {
             const int row = IO::local_row(t, i);
             for (int tt = 0; tt < n; ++tt) {
-                const float g = g_l[tt];
                 const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
                 const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
                 const float d = d_l[tt * kRows + row];
+                if constexpr (CH) {
+                    const f32x4 al0 = ld4(g_l + tt * kDim + c0);
+                    const f32x4 al1 = ld4(g_l + tt * kDim + c0 + 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * g);
-                    h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * g);
+                    for (int e = 0; e < 4; ++e) {
+                        h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * al0[e]);
+                        h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * al1[e]);
+                    }
+                } else {
+                    const float g = g_l[tt];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * g);
+                        h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * g);
+                    }
                 }
                 if constexpr (ALIGN) {
                     if (tt + 1 == bl) {
@@ -462,14 +494,16 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
     void* kargs[] = {&args};
     args.ssm_wgs = p.hv > 0 ? (int64_t)p.num_layers * p.num_rows * p.hv * SPLIT : 0;
     const uint64_t grid = (uint64_t)(args.ssm_wgs + p.conv_wgs);
+    const bool conv = p.conv_wgs > 0;
     const void* fn =
-        p.payload ? (p.conv_wgs > 0
-                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, true>)
-                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, true>))
-                  : (p.conv_wgs > 0
-                         ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, false>)
-                         : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false>));
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, commit_lds_bytes(p.T), s);
+        p.payload   ? (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, true, false>)
+                            : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, true, false>))
+        : p.channel ? (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, false, true>)
+                            : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false, true>))
+                    : (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, false, false>)
+                            : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false, false>));
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs,
+                           commit_lds_bytes(p.T, p.channel), s);
 }
 
 // Workgroups per head: the splits the launch chooses from (8 KiB per workgroup

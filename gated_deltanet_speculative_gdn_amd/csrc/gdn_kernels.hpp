@@ -34,6 +34,8 @@ struct VerifyParams {
     bool raw_gates;           // gates from raw a, b with A_log, dt_bias
     bool out_bf16;            // outputs rounded to bf16 (nearest even)
     bool payload;             // payload records (k, v, gate, beta) instead of corrections
+    bool channel;             // one decay per key channel: a_log is [tokens][HV][K] with
+    int64_t a_ts;             //   token stride a_ts; records hold alpha[T][K] for the gate
     int32_t lds_floor;        // launch: at least this much dynamic LDS (bytes; 0 = the default)
 };
 
@@ -66,6 +68,7 @@ struct CommitParams {
     int64_t rec_stride;
     int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
     bool payload;             // payload records: the replay recomputes the corrections
+    bool channel;             // per-channel decay records: alpha[T][K] in place of the gate
     int64_t ssm_wgs;          // workgroups of the state replay (the first ones of the grid)
     int64_t conv_wgs;         // workgroups of the conv compaction (after them; 0 = none)
     ConvParams conv;
@@ -124,6 +127,9 @@ hipError_t launch_commit(const CommitParams& p, bool bf16_state, bool align, hip
 hipError_t launch_native_accept(const AcceptParams& p, bool bf16_state, hipStream_t s);
 hipError_t launch_align_plan(const PlanParams& p, hipStream_t s);
 
-inline size_t commit_lds_bytes(int T) { return sizeof(float) * (2 * (size_t)T * 128 + 2 * (size_t)T); }
+inline size_t commit_lds_bytes(int T, bool channel = false)
+{
+    return sizeof(float) * ((channel ? 3 : 2) * (size_t)T * 128 + 2 * (size_t)T);
+}
 
 }  // namespace gdn

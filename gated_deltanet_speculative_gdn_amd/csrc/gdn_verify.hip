@@ -135,19 +135,26 @@ __device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x,
 // Only the keys and queries are needed whole (the dot products); keeping the
 // row-indexed fields to the owned rows lets more workgroups share a CU at long
 // record capacities.
-template <int TT, int RW> struct Lds {
-    static constexpr size_t kFloats = 2 * TT * kDim + 3 * TT * RW + 3 * TT + 2 * TT * TT;
-    float *khat, *qt, *vd, *dw, *ob, *g, *be, *g0, *ca, *cb;
+// With one decay per key channel (CH) three more [TT][128] arrays follow:
+//   al  the decays of every position;  kx, qx  the window's keys and queries
+//   scaled channel by channel by the decay products G(0, p+1), the vectors the
+//   checkpoint is contracted with (the scalar G(0, p+1) of the scalar-decay
+//   rule is then 1).
+template <int TT, int RW, bool CH = false> struct Lds {
+    static constexpr size_t kFloats =
+        2 * TT * kDim + 3 * TT * RW + 3 * TT + 2 * TT * TT + (CH ? 3 * TT * kDim : 0);
+    float *khat, *qt, *vd, *dw, *ob, *g, *be, *g0, *ca, *cb, *al, *kx, *qx;
     __device__ explicit Lds(float* base)
         : khat(base), qt(base + TT * kDim), vd(base + 2 * TT * kDim), dw(vd + TT * RW),
-          ob(dw + TT * RW), g(ob + TT * RW), be(g + TT), g0(be + TT), ca(g0 + TT), cb(ca + TT * TT) {}
+          ob(dw + TT * RW), g(ob + TT * RW), be(g + TT), g0(be + TT), ca(g0 + TT), cb(ca + TT * TT),
+          al(cb + TT * TT), kx(al + TT * kDim), qx(kx + TT * kDim) {}
 };
 
 // NT threads per workgroup, R rows of the head per thread: a workgroup covers
 // NT/8 * R rows, so a head is split over kChunks workgroups. Each stages the
 // whole window (the norms and dot products need all 128 columns); the
 // head-level record fields (key, gate) are written by the first chunk.
-template <typename StateT, bool SNAP, int R, int NT, int TT>
+template <typename StateT, bool SNAP, int R, int NT, int TT, bool CH>
 __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 {
     static_assert(R == 1 || R == 2 || R == 4, "rows per thread");
@@ -156,7 +163,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     constexpr int kChunks = kDim / kRowsPerWg;
     extern __shared__ float lds_raw[];
     const int T = p.T;   // record capacity (record addressing); T <= TT
-    const Lds<TT, kRowsPerWg> L(lds_raw);
+    const Lds<TT, kRowsPerWg, CH> L(lds_raw);
 
     const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int chunk = (int)(item % kChunks);
@@ -218,8 +225,23 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     // gate inputs of token min(tid, w-1): unconditional, so no use of them is
     // hoisted above the tile loads below
     const int64_t gtok = (int64_t)ts + (tid < w ? tid : w - 1);
-    const float a_in = p.a_log[gtok * p.g_ts + hv];
+    float a_in = 0.f;
+    if constexpr (!CH) a_in = p.a_log[gtok * p.g_ts + hv];
     const float b_in = p.beta[gtok * p.g_ts + hv];
+    // per-channel log-decays of the window's tokens (CH): 32 16-byte pieces a token
+    constexpr int kAChunks = CH ? (TT * (kDim / 4) + NT - 1) / NT : 1;
+    f32x4 win_a[kAChunks];
+    if constexpr (CH) {
+        const float* a_base = p.a_log + (int64_t)ts * p.a_ts + (int64_t)hv * kDim;
+#pragma unroll
+        for (int q = 0; q < kAChunks; ++q) {
+            const int i = tid + q * NT;
+            if (i < w * (kDim / 4)) {
+                const int t = i / (kDim / 4);
+                win_a[q] = ld4(a_base + t * p.a_ts + 4 * (i - t * (kDim / 4)));
+            }
+        }
+    }
     // per-head gate parameters (raw gates); otherwise a harmless in-bounds read
     const float alog_in = (p.raw_gates ? p.A_log : p.a_log)[hv];
     const float dtb_in = (p.raw_gates ? p.dt_bias : p.beta)[hv];
@@ -229,7 +251,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     constexpr int kRowQ = kRowsPerWg / 4;
     constexpr int kRingD = (kMaxRecTokens * kRowQ + NT - 1) / NT;
     constexpr int kRingK = (kMaxRecTokens * (kDim / 4) + NT - 1) / NT;
-    f32x4 ring_d[kRingD], ring_k[kRingK];
+    f32x4 ring_d[kRingD], ring_k[kRingK], ring_a[CH ? kRingK : 1];
     float ring_g = 0.f;
     if constexpr (!SNAP) {
         recb = p.rec + ((int64_t)rs * p.hv + hv) * p.rec_stride;
@@ -246,7 +268,15 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             const int i = tid + q * NT;
             if (i < j0 * (kDim / 4)) ring_k[q] = ld4(recb + (int64_t)T * kDim + 4 * i);
         }
-        if (tid < j0) ring_g = recb[2 * (int64_t)T * kDim + tid];
+        if constexpr (CH) {   // the pending positions' per-channel decays
+#pragma unroll
+            for (int q = 0; q < kRingK; ++q) {
+                const int i = tid + q * NT;
+                if (i < j0 * (kDim / 4)) ring_a[q] = ld4(recb + 2 * (int64_t)T * kDim + 4 * i);
+            }
+        } else {
+            if (tid < j0) ring_g = recb[2 * (int64_t)T * kDim + tid];
+        }
     }
     const StateT* head = static_cast<const StateT*>(p.state) + ((int64_t)slot * p.hv + hv) * kHeadElems;
     f32x4 h[R][4];
@@ -267,7 +297,29 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             const int i = tid + q * NT;
             if (i < j0 * (kDim / 4)) st4(L.khat + 4 * i, ring_k[q]);
         }
-        if (tid < j0) L.g[tid] = ring_g;
+        if constexpr (CH) {
+#pragma unroll
+            for (int q = 0; q < kRingK; ++q) {
+                const int i = tid + q * NT;
+                if (i < j0 * (kDim / 4)) st4(L.al + 4 * i, ring_a[q]);
+            }
+        } else {
+            if (tid < j0) L.g[tid] = ring_g;
+        }
+    }
+    if constexpr (CH) {   // the window's per-channel decays, and their record (lead chunk)
+#pragma unroll
+        for (int q = 0; q < kAChunks; ++q) {
+            const int i = tid + q * NT;
+            if (i < w * (kDim / 4)) {
+                const int t = i / (kDim / 4);
+                const int off = (j0 + t) * kDim + 4 * (i - t * (kDim / 4));
+                const f32x4 al = f32x4{expf(win_a[q].x), expf(win_a[q].y), expf(win_a[q].z),
+                                       expf(win_a[q].w)};
+                st4(L.al + off, al);
+                if (!SNAP && lead) st4(recb + 2 * (int64_t)T * kDim + off, al);
+            }
+        }
     }
     for (int jb = jb0; jb < 3 * w; jb += NT / 16) {
         const int t = jb / 3;
@@ -310,8 +362,12 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         float av = a_in, bv = b_in;
         if (t != tid) {          // windows longer than the workgroup (not reachable at T <= 16)
             const int64_t tok = (int64_t)ts + t;
-            av = p.a_log[tok * p.g_ts + hv];
+            if constexpr (!CH) av = p.a_log[tok * p.g_ts + hv];
             bv = p.beta[tok * p.g_ts + hv];
+        }
+        if constexpr (CH) {      // the decays are per channel (staged above); beta as given
+            L.be[j0 + t] = bv;
+            continue;
         }
         float g, be;
         if (p.raw_gates) {
@@ -355,25 +411,70 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         const int j = is_q ? rem - pp : rem;
         const float* a = L.khat + j * kDim + 8 * lane16;
         const float* c = (is_q ? L.qt : L.khat) + pp * kDim + 8 * lane16;
-        const f32x4 a0 = ld4(a), a1 = ld4(a + 4), c0 = ld4(c), c1 = ld4(c + 4);
+        f32x4 a0 = ld4(a), a1 = ld4(a + 4);
+        const f32x4 c0 = ld4(c), c1 = ld4(c + 4);
+        if constexpr (CH) {
+            // k_j weighted channel by channel by the decays of positions j+1 .. pp
+            f32x4 w0 = {1.f, 1.f, 1.f, 1.f}, w1 = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int m = 1; m < TT; ++m)
+                if (m > j && m <= pp) {
+                    const f32x4 x0 = ld4(L.al + m * kDim + 8 * lane16), x1 = ld4(L.al + m * kDim + 8 * lane16 + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        w0[e] = w0[e] * x0[e];
+                        w1[e] = w1[e] * x1[e];
+                    }
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a0[e] = a0[e] * w0[e];
+                a1[e] = a1[e] * w1[e];
+            }
+        }
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a0[e], c0[e], dot);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dot = __builtin_fmaf(a1[e], c1[e], dot);
         dot = sum16(dot);
-        float gam = 1.f;                  // g_{j+1} ... g_pp, in that order
+        if constexpr (CH) {
+            if (lane16 == 0) (is_q ? L.cb : L.ca)[j * TT + pp] = dot;
+        } else {
+            float gam = 1.f;              // g_{j+1} ... g_pp, in that order
 #pragma unroll
-        for (int m = 1; m < TT; ++m)
-            if (m > j && m <= pp) gam = gam * gv[m];
-        if (lane16 == 0) (is_q ? L.cb : L.ca)[j * TT + pp] = gam * dot;
+            for (int m = 1; m < TT; ++m)
+                if (m > j && m <= pp) gam = gam * gv[m];
+            if (lane16 == 0) (is_q ? L.cb : L.ca)[j * TT + pp] = gam * dot;
+        }
     }
-    for (int t = tid; t < w; t += NT) {
-        float gam = 1.f;                  // g_0 ... g_{j0+t}, in that order
+    if constexpr (CH) {
+        // the vectors the checkpoint meets: k_p and q_p scaled channel by
+        // channel by the decays of positions 0 .. p, in that order
+        for (int i = tid; i < w * (kDim / 4); i += NT) {
+            const int pp = j0 + i / (kDim / 4);
+            const int c = 4 * (i % (kDim / 4));
+            f32x4 gam = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int m = 0; m < TT; ++m)
-            if (m <= j0 + t) gam = gam * gv[m];
-        L.g0[j0 + t] = gam;
+            for (int m = 0; m < TT; ++m)
+                if (m <= pp) {
+                    const f32x4 x = ld4(L.al + m * kDim + c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gam[e] = gam[e] * x[e];
+                }
+            const f32x4 kv = ld4(L.khat + pp * kDim + c), qv = ld4(L.qt + pp * kDim + c);
+            st4(L.kx + pp * kDim + c, f32x4{gam.x * kv.x, gam.y * kv.y, gam.z * kv.z, gam.w * kv.w});
+            st4(L.qx + pp * kDim + c, f32x4{gam.x * qv.x, gam.y * qv.y, gam.z * qv.z, gam.w * qv.w});
+        }
+        for (int t = tid; t < w; t += NT) L.g0[j0 + t] = 1.f;
+    } else {
+        for (int t = tid; t < w; t += NT) {
+            float gam = 1.f;              // g_0 ... g_{j0+t}, in that order
+#pragma unroll
+            for (int m = 0; m < TT; ++m)
+                if (m <= j0 + t) gam = gam * gv[m];
+            L.g0[j0 + t] = gam;
+        }
     }
     __syncthreads();
 
@@ -391,7 +492,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         if (pp >= P) break;
         const float g0 = L.g0[pp];
         float pk[R];
-        tile_dot<R>(h, L.khat + pp * kDim, lane8, pk);
+        tile_dot<R>(h, (CH ? L.kx : L.khat) + pp * kDim, lane8, pk);
         float u[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) u[r] = g0 * pk[r];
@@ -408,7 +509,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int r = 0; r < R; ++r) L.dw[pp * kRowsPerWg + rl + r] = dreg[pp][r];  // same value in all 8 lanes
 
         float pq[R];
-        tile_dot<R>(h, L.qt + pp * kDim, lane8, pq);
+        tile_dot<R>(h, (CH ? L.qx : L.qt) + pp * kDim, lane8, pq);
         float o[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = g0 * pq[r];
@@ -446,16 +547,19 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int t = 0; t < TT; ++t) {
             if (t >= w) break;
             const float g = L.g[t];
-            f32x4 kh[4];
+            f32x4 kh[4], dc[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
+            for (int c = 0; c < 4; ++c) {
+                kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
+                dc[c] = CH ? ld4(L.al + t * kDim + 4 * lane8 + 32 * c) : f32x4{g, g, g, g};
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float d = dreg[t][r];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[r][c][e] = __builtin_fmaf(d, kh[c][e], h[r][c][e] * g);
+                    for (int e = 0; e < 4; ++e) h[r][c][e] = __builtin_fmaf(d, kh[c][e], h[r][c][e] * dc[c][e]);
             }
             StateT* sn = static_cast<StateT*>(p.snap) + (((int64_t)b * p.hv + hv) * T + t) * kHeadElems;
             TileIO<StateT, R>::store(sn, row0, grp, lane8, h);
@@ -463,27 +567,33 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     }
 }
 
-template <typename StateT, bool SNAP, int R, int NT, int TT>
+template <typename StateT, bool SNAP, int R, int NT, int TT, bool CH>
 hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
 {
     VerifyParams args = p;
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
-    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R>::kFloats;
+    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R, CH>::kFloats;
     const size_t lds = need > (size_t)p.lds_floor ? need : (size_t)p.lds_floor;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT, CH>),
                            dim3(grid), dim3(NT), kargs, lds, s);
 }
 
 // The smallest compile-time window capacity that holds the record capacity.
+template <typename StateT, bool SNAP, bool CH>
+hipError_t launch_ch(const VerifyParams& p, hipStream_t s)
+{
+    constexpr int R = kVerifyRowsPerThread, NT = kVerifyThreads;
+    if (p.T <= 4) return launch_tt<StateT, SNAP, R, NT, 4, CH>(p, s);
+    if (p.T <= 8) return launch_tt<StateT, SNAP, R, NT, 8, CH>(p, s);
+    return launch_tt<StateT, SNAP, R, NT, kMaxRecTokens, CH>(p, s);
+}
+
 template <typename StateT, bool SNAP>
 hipError_t launch(const VerifyParams& p, hipStream_t s)
 {
-    constexpr int R = kVerifyRowsPerThread, NT = kVerifyThreads;
-    if (p.T <= 4) return launch_tt<StateT, SNAP, R, NT, 4>(p, s);
-    if (p.T <= 8) return launch_tt<StateT, SNAP, R, NT, 8>(p, s);
-    return launch_tt<StateT, SNAP, R, NT, kMaxRecTokens>(p, s);
+    return p.channel ? launch_ch<StateT, SNAP, true>(p, s) : launch_ch<StateT, SNAP, false>(p, s);
 }
 
 }  // namespace

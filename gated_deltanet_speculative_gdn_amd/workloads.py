@@ -246,6 +246,21 @@ def make_raw_gates(wl: Workload, device="cpu", seed: int | None = None) -> RawGa
     return RawGates(*(torch.as_tensor(x, device=dev) for x in (a, b, A_log, dt_bias)))
 
 
+CHANNEL_DECAY_SEED_OFFSET = 65537
+
+
+def make_channel_decays(wl: Workload, device="cpu", seed: int | None = None) -> torch.Tensor:
+    """One log-decay per (layer, token, value head, key channel), fp32
+    [L][tokens][HV][128], drawn like the scalar log-gate (-softplus of a
+    standard normal) from a stream of its own."""
+    s = wl.spec
+    seed = (s.seed if seed is None else seed) + CHANNEL_DECAY_SEED_OFFSET
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((s.layers, wl.tokens, s.hv, 128), dtype=np.float32)
+    a = -np.logaddexp(np.float32(0), x).astype(np.float32)
+    return torch.as_tensor(a, device=torch.device(device))
+
+
 @dataclass
 class ConvInputs:
     """Short-conv state pools of every layer and the step's conv inputs."""

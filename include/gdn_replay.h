@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 #define GDN_MAX_LAYERS 64      /* layers per pool set */
 #define GDN_HEAD_DIM 128       /* K = V = 128 */
 #define GDN_MAX_REC_TOKENS 16  /* record capacity T per row */
@@ -69,8 +69,9 @@ typedef enum {
 } gdn_status;
 
 typedef enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 } gdn_state_dtype;
-typedef enum { GDN_GATE_LOG = 0, GDN_GATE_RAW = 1 } gdn_gate_mode;
-typedef enum { GDN_RECORD_CORRECTION = 0, GDN_RECORD_PAYLOAD = 1 } gdn_record_kind;
+typedef enum { GDN_GATE_LOG = 0, GDN_GATE_RAW = 1, GDN_GATE_CHANNEL = 2 } gdn_gate_mode;
+typedef enum { GDN_RECORD_CORRECTION = 0, GDN_RECORD_PAYLOAD = 1, GDN_RECORD_CHANNEL = 2 }
+    gdn_record_kind;
 typedef enum { GDN_OUT_F32 = 0, GDN_OUT_BF16 = 1 } gdn_out_dtype;
 
 /* Device row-error bits (OR'ed into *err_flags). */
@@ -102,6 +103,12 @@ enum {
  *     recomputes the corrections, reductions included):
  *     k[T][K] bf16 (the key head's raw key) | v[T][V] bf16 | gate[T] fp32 |
  *     beta[T] fp32 | padding to 16 bytes.
+ *   GDN_RECORD_CHANNEL (the per-key-channel decay reading of Kimi-K3 KDA,
+ *     which the pages name as a user of the same protocol without giving its
+ *     arithmetic: the scalar decay becomes one decay per key channel), fp32:
+ *     delta[T][V] | k_hat[T][K] | alpha[T][K]; it goes with gate_mode
+ *     GDN_GATE_CHANNEL and the commit replays
+ *     h[v][k] = fma(delta_t[v], k_hat_t[k], h[v][k] * alpha_t[k]).
  *   The payload record cannot serve ring mode (pending records would need
  *   their corrections), so verify rejects a rec_base with it.
  */
@@ -137,7 +144,13 @@ typedef struct gdn_pools {
  *       softplus(x) = x for x > 20, else log(1 + exp(x)). This parameterisation
  *       is not printed on the pages; it is the decay/write-strength form used
  *       with Gated DeltaNet layers ([GDN]).
- *     Either way the record holds the decay g that was multiplied in.
+ *     gate_mode GDN_GATE_CHANNEL (pools->record_kind GDN_RECORD_CHANNEL, and
+ *       only then): a is one log-decay per key channel, device fp32
+ *       [tokens][HV][K] at a[tok * decay_tok_stride + h * K + k] (16-byte
+ *       aligned, decay_tok_stride a multiple of 4 and >= HV * K), the decay of
+ *       channel k is alpha[k] = exp(a[..k]) and h' = h * alpha column by
+ *       column; b is beta as in GDN_GATE_LOG.
+ *     Either way the record holds the decay that was multiplied in.
  *   out: device [tokens][HV][V], fp32 (out_dtype GDN_OUT_F32; 16-byte aligned,
  *     strides multiples of 4) or bf16 bits rounded to nearest even once
  *     (GDN_OUT_BF16; 8-byte aligned, strides multiples of 4).
@@ -157,6 +170,7 @@ typedef struct gdn_verify_io {
     const float* dt_bias;   /* GDN_GATE_RAW only, else ignored */
     int32_t out_dtype;      /* gdn_out_dtype */
     int32_t reserved;       /* set to 0 */
+    int64_t decay_tok_stride;  /* GDN_GATE_CHANNEL only: token stride of a, else ignored */
 } gdn_verify_io;
 
 /*
@@ -191,7 +205,8 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
  * arrays [num_rows]):
  *   n = n_accept[b]; if n == 0 or src_slot[b] < 0 nothing is read or written.
  *   h = state[l][src_slot[b]]; for t < n: h = fma(delta_t, k_hat_t^T, h * g_t)
- *   with the records of rec_slot[b]; the final h is written to dst_slot[b]
+ *   with the records of rec_slot[b] (per-channel decay records: h * alpha_t
+ *   column by column; payload records: the correction recomputed first); the final h is written to dst_slot[b]
  *   (dst == src: in place). bf16 pools round once, to nearest even, here.
  *   Align mode (bnd_len and bnd_slot non-NULL): when 0 < bnd_len[b] < n the
  *   state after bnd_len[b] tokens is also written to bnd_slot[b], after the
@@ -349,9 +364,9 @@ int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers,
  * T*(V+K) + T rounded up to 4 (0 for T < 1). */
 int64_t gdn_rec_stride(int32_t rec_tokens);
 
-/* Floats per (record slot, value head) block of either record kind
- * (payload: (T*(K+V)*2 + 8*T) bytes rounded up to 16, in floats); 0 for
- * T < 1 or an unknown kind. */
+/* Floats per (record slot, value head) block of a record kind (payload:
+ * (T*(K+V)*2 + 8*T) bytes rounded up to 16, in floats; per-channel decay:
+ * T*(V+2K)); 0 for T < 1 or an unknown kind. */
 int64_t gdn_record_stride(int32_t rec_tokens, int32_t record_kind);
 
 const char* gdn_status_string(int32_t status);

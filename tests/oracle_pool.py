@@ -96,3 +96,28 @@ def relerr_blocks(x: np.ndarray, y: np.ndarray, block_shape_ndim: int) -> float:
     den = np.abs(y).max(axis=axes)
     den = np.where(den == 0, 1.0, den)
     return float((num / den).max())
+
+
+def gather_channel_decays(wl, a_ch, layer, rows, T=None) -> np.ndarray:
+    """Per-channel log-decays [R*HV][T][K] of ``rows`` from a [L][tokens][HV][K]
+    tensor, packed like :func:`gather`'s heads."""
+    s = wl.spec
+    rows = np.asarray(rows)
+    tok = token_index(wl, rows, T)
+    R, T = len(rows), tok.shape[1]
+    tix = torch.as_tensor(tok.reshape(-1).astype(np.int64), device=a_ch.device)
+    a = to_f32(a_ch[layer].index_select(0, tix)).reshape(R, T, s.hv, s.dk)
+    return np.ascontiguousarray(a.transpose(0, 2, 1, 3)).reshape(R * s.hv, T, s.dk)
+
+
+def run_layer_ch(wl, a_ch, layer, rows, *, keep=None, scale=1.0, T=None, snaps=False,
+                 dtype=np.float32, state=None):
+    """Oracle rule with one decay per key channel for ``rows`` of ``layer``."""
+    g = gather(wl, layer, rows, T, state)
+    g["a"] = gather_channel_decays(wl, a_ch, layer, rows, T)
+    keep_h = None
+    if keep is not None:
+        keep_h = np.repeat(np.asarray(keep, np.int32).reshape(len(rows), -1), wl.spec.hv, axis=0)
+    res = oracle.native_heads_ch(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
+                                 scale=scale, keep=keep_h, snaps=snaps, dtype=dtype)
+    return g, res

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.gdn_status_string(s), bytes)
     assert lib.gdn_status_string(-4).decode().startswith("a pointer or stride")
@@ -60,8 +60,12 @@ def test_payload_record_stride(lib):
     assert lib.gdn_record_stride(1, 1) == 528 // 4
     assert lib.gdn_record_stride(16, 1) == 16 * 520 // 4
     assert lib.gdn_record_stride(4, 0) == lib.gdn_rec_stride(4)
-    assert lib.gdn_record_stride(4, 2) == 0
+    # per-channel decay records: delta[T][128] | k_hat[T][128] | alpha[T][128]
+    assert lib.gdn_record_stride(4, 2) == 4 * 384
+    assert lib.gdn_record_stride(16, 2) == 16 * 384
+    assert lib.gdn_record_stride(4, 3) == 0
     assert lib.gdn_record_stride(0, 1) == 0
+    assert lib.gdn_record_stride(0, 2) == 0
 
 
 def good_pools():
@@ -110,7 +114,10 @@ def test_verify_zero_rows_is_ok_without_launch(lib):
     (lambda p, io: setattr(p, "rec_tokens", 17), E_SHAPE),
     (lambda p, io: setattr(p, "num_state_slots", 0), E_SHAPE),
     (lambda p, io: setattr(p, "state_dtype", 2), E_DTYPE),
-    (lambda p, io: setattr(p, "record_kind", 2), E_SHAPE),
+    (lambda p, io: setattr(p, "record_kind", 3), E_SHAPE),
+    (lambda p, io: setattr(p, "record_kind", 2), E_SHAPE),    # channel records, scalar gates
+    (lambda p, io: setattr(io, "gate_mode", 2), E_SHAPE),     # channel gates, scalar records
+    (lambda p, io: setattr(io, "gate_mode", 3), E_SHAPE),
     (lambda p, io: p.state.__setitem__(0, 0), E_NULL),
     (lambda p, io: p.rec.__setitem__(0, 0), E_NULL),
     (lambda p, io: p.state.__setitem__(0, 0x10004), E_ALIGN),
@@ -145,6 +152,24 @@ def test_verify_accepts_raw_gates_and_bf16_out(lib):
     io.gate_mode, io.A_log, io.dt_bias = 1, 0x90000, 0x90100
     io.out_dtype, io.out = 1, 0x80008          # bf16 output: 8-byte pieces
     assert verify(lib, good_pools(), io, rows=0) == OK
+
+
+def test_verify_channel_decays(lib):
+    """Per-channel decays need the channel record kind, a 16-byte aligned a and
+    a token stride of at least HV * 128 in multiples of 4."""
+    p = good_pools()
+    p.record_kind = 2
+    io = good_io()
+    io.gate_mode, io.decay_tok_stride = 2, 4 * 128
+    assert verify(lib, p, io, rows=0) == OK
+    io.decay_tok_stride = 4 * 128 - 4
+    assert verify(lib, p, io) == E_SHAPE
+    io.decay_tok_stride = 4 * 128 + 2
+    assert verify(lib, p, io) == E_ALIGN
+    io.decay_tok_stride, io.a = 4 * 128, 0x60004
+    assert verify(lib, p, io) == E_ALIGN
+    io.a, io.decay_tok_stride = 0x60000, -4
+    assert verify(lib, p, io) == E_SHAPE
 
 
 def test_payload_records_reject_a_ring_base(lib):
