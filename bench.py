@@ -35,6 +35,8 @@ from gated_deltanet_speculative_gdn_amd import workloads as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 REC_TOKEN_BYTES = (128 + 128 + 1) * 4           # correction, key, gate (fp32)
 PAYLOAD_TOKEN_BYTES = (128 + 128) * 2 + 2 * 4    # raw key, raw value (bf16), gate, beta (fp32)
+CHANNEL_TOKEN_BYTES = (128 + 128 + 128) * 4      # correction, key, per-channel decays (fp32)
+CHANNEL_GATE_BYTES = 128 * 4 + 4                 # per-channel log-decays and beta, per head
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "commit_counters.json")
 KERNEL_SOURCES = ["gated_deltanet_speculative_gdn_amd/csrc/gdn_commit.hip",
                   "gated_deltanet_speculative_gdn_amd/csrc/gdn_device.hpp",
@@ -68,6 +70,9 @@ class Step:
 
     def __init__(self, wl, raw_gates=False, out_dtype=torch.float32, conv=None,
                  record_kind=G.RECORD_CORRECTION):
+        # per-key-channel decays go with their own record kind
+        self.a_ch = W.make_channel_decays(wl, device="cuda") \
+            if record_kind == G.RECORD_CHANNEL else None
         s = wl.spec
         self.wl, self.s = wl, s
         self.rec = G.Pools.alloc_records(s.layers, s.rows, s.hv, s.rec_tokens,
@@ -94,6 +99,8 @@ class Step:
     def gates(self, layer):
         """(a, b, keyword arguments) of the layer's verify: log-gate and beta,
         or the raw projections with the per-head gate parameters."""
+        if self.a_ch is not None:
+            return self.a_ch[layer], self.wl.beta[layer], {}
         if self.rg is None:
             return self.wl.a[layer], self.wl.beta[layer], {}
         rg = self.rg
@@ -148,7 +155,8 @@ class Step:
         G.gdn_native_accept(self.pools, self.snaps, self.slot, self.n, err_flags=self.err)
 
 
-def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_BYTES):
+def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_BYTES,
+               gate_bytes=8):
     """Update counts and algorithmic HBM bytes of one step (out_bytes: bytes
     per output element; raw gates add the per-head parameters; conv: the
     short-conv states compacted in the commit launch)."""
@@ -160,7 +168,7 @@ def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_
     steps = max(s.ring_steps, 1)
     verify_updates = int(s.layers * s.hv * w.sum() * steps)
     commit_updates = int(s.layers * s.hv * n.sum())
-    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + 8 + 128 * out_bytes + rec_bytes)
+    per_tok = s.hk * 2 * 128 * 2 + s.hv * (128 * 2 + gate_bytes + 128 * out_bytes + rec_bytes)
     verify_bytes_layer = int(real.sum() * s.hv * sb + w.sum() * per_tok + (s.hv * 8 if raw_gates else 0))
     if s.ring_steps:
         # average launch of the ring: step j also reads j pending records per head
@@ -213,11 +221,12 @@ def capture(fn):
     return g
 
 
-def cpu_baseline(wl, acc, target_s=15.0):
+def cpu_baseline(wl, acc, target_s=15.0, a_ch=None):
     """The oracle (plain C, OpenMP over heads) on the same workload: every
     layer's real rows, windows and accepted counts, the whole step repeated
     until about `target_s` seconds of oracle time (the count is fixed from the
-    first layer's time)."""
+    first layer's time). a_ch: per-key-channel log-decays, when the step runs
+    with them."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     import oracle_pool as OP
@@ -226,26 +235,30 @@ def cpu_baseline(wl, acc, target_s=15.0):
     nthreads = oracle.default_threads()
     keep = np.repeat(wl.n_accept[real], s.hv)[:, None]
 
-    def run(g):
+    native = oracle.native_heads if a_ch is None else oracle.native_heads_ch
+
+    def gather(layer):
+        g = OP.gather(wl, layer, real)
+        if a_ch is not None:
+            g["a"] = OP.gather_channel_decays(wl, a_ch, layer, real)
+        return g
+
+    def run(g, threads=nthreads):
         t0 = time.perf_counter()
-        oracle.native_heads(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
-                            keep=keep, nthreads=nthreads)
+        native(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"], keep=keep,
+               nthreads=threads)
         return time.perf_counter() - t0
 
-    g = OP.gather(wl, 0, real)
+    g = gather(0)
     first = run(g)
     reps = max(1, int(np.ceil(target_s / (first * s.layers))))
     spent = first + sum(run(g) for _ in range(reps - 1))
     for layer in range(1, s.layers):
-        g = OP.gather(wl, layer, real)
+        g = gather(layer)
         spent += sum(run(g) for _ in range(reps))
     updates = reps * (acc["verify_updates"] + acc["commit_updates"])
     # one thread, on the first layer only (a bounded sample of the same rule)
-    g = OP.gather(wl, 0, real)
-    t0 = time.perf_counter()
-    oracle.native_heads(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
-                        keep=keep, nthreads=1)
-    one = time.perf_counter() - t0
+    one = run(gather(0), threads=1)
     single = (acc["verify_updates"] + acc["commit_updates"]) / s.layers / one
     return {"value": updates / spent, "unit": "state-updates/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(spent, 3), "cpu_model": cpu_model(),
@@ -286,9 +299,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.MTP_B64.name, choices=sorted(W.WORKLOADS))
     ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
-    ap.add_argument("--gating", default="log", choices=["log", "raw"],
+    ap.add_argument("--gating", default="log", choices=["log", "raw", "channel"],
                     help="log: log-gate and beta given; raw: gates formed in the kernel from "
-                         "raw a, b with per-head A_log, dt_bias")
+                         "raw a, b with per-head A_log, dt_bias; channel: one log-decay per key "
+                         "channel (records keep the decays per channel)")
     ap.add_argument("--out-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--record", default="correction", choices=["correction", "payload"],
                     help="correction: (delta, k_hat, gate) records, elementwise commit; payload: "
@@ -311,6 +325,10 @@ def main():
     if spec.ring_steps and (args.record == "payload" or args.conv):
         print("the ring workload needs correction records and no conv states", file=sys.stderr)
         sys.exit(2)
+    if args.gating == "channel" and args.record == "payload":
+        print("per-channel decays keep their own record kind, not the payload record",
+              file=sys.stderr)
+        sys.exit(2)
     torch.cuda.set_device(0)
     G.load_library()
     dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
@@ -318,12 +336,16 @@ def main():
     wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
     conv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if args.conv else None
     payload = args.record == "payload"
+    channel = args.gating == "channel"
     acc = accounting(wl, out_bytes=2 if args.out_dtype == "bf16" else 4,
                      raw_gates=args.gating == "raw", conv=conv,
-                     rec_bytes=PAYLOAD_TOKEN_BYTES if payload else REC_TOKEN_BYTES)
+                     rec_bytes=(PAYLOAD_TOKEN_BYTES if payload else
+                                CHANNEL_TOKEN_BYTES if channel else REC_TOKEN_BYTES),
+                     gate_bytes=CHANNEL_GATE_BYTES if channel else 8)
     st = Step(wl, raw_gates=args.gating == "raw",
               out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32, conv=conv,
-              record_kind=G.RECORD_PAYLOAD if payload else G.RECORD_CORRECTION)
+              record_kind=(G.RECORD_PAYLOAD if payload else
+                           G.RECORD_CHANNEL if channel else G.RECORD_CORRECTION))
     L = spec.layers
 
     # warm-up (also loads the code object before capture)
@@ -388,7 +410,7 @@ def main():
                    "padding_rows": spec.pad_rows, "value_heads": spec.hv, "key_heads": spec.hk,
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
                    "gating": args.gating, "out_dtype": args.out_dtype, "conv_states": args.conv,
-                   "record": args.record, "ring_steps": spec.ring_steps, "block": spec.block,
+                   "record": "channel" if channel else args.record, "ring_steps": spec.ring_steps, "block": spec.block,
                    "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
         "roofline": roofline,
         "kernels": {
@@ -487,7 +509,7 @@ def main():
 
     if not args.no_cpu:
         log("timing the CPU oracle on one full step ...")
-        result["cpu_baseline"] = cpu_baseline(wl, acc)
+        result["cpu_baseline"] = cpu_baseline(wl, acc, a_ch=st.a_ch)
     print(json.dumps(result), flush=True)
 
 

@@ -29,8 +29,10 @@
 // pages' read-after-overwrite race between programs cannot occur.
 //
 // The same launch optionally carries the short conv's state compaction (extra
-// workgroups after the replay's) and serves the payload record kind, whose
-// replay recomputes each correction from the recorded key and value.
+// workgroups after the replay's) and serves two more record kinds: the payload
+// kind, whose replay recomputes each correction from the recorded key and
+// value, and the per-key-channel decay kind (a reading of Kimi-K3 KDA), whose
+// replay is h[v][k] = fma(delta[v], k_hat[k], h[v][k] * alpha[k]).
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 

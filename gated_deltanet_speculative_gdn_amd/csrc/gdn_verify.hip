@@ -40,7 +40,13 @@
 //
 // Options carried in the parameters: gates formed here from raw projections
 // (A_log, dt_bias), outputs rounded to bf16, and payload records (the raw key
-// and value with the gates) in place of the corrections.
+// and value with the gates) in place of the corrections. A template flag (CH)
+// takes one decay per key channel (a reading of Kimi-K3 KDA, which the vLLM
+// PR's Purpose names as a user of the same protocol): the decay products
+// become elementwise, G(a, b) = alpha_a * ... * alpha_{b-1} per channel, so
+// S0 is contracted with G(0,p+1) * k_p and G(0,p+1) * q_p and each
+// coefficient is the dot product of k_j * G(j+1,p+1) with k_p or q_p; the
+// record keeps alpha[K] in place of the gate.
 //
 // The native baseline is the same template with SNAP = true: the same
 // corrections and outputs, bit for bit, then the states S_1..S_w materialised

@@ -103,9 +103,9 @@ enum {
  *     recomputes the corrections, reductions included):
  *     k[T][K] bf16 (the key head's raw key) | v[T][V] bf16 | gate[T] fp32 |
  *     beta[T] fp32 | padding to 16 bytes.
- *   GDN_RECORD_CHANNEL (the per-key-channel decay reading of Kimi-K3 KDA,
- *     which the pages name as a user of the same protocol without giving its
- *     arithmetic: the scalar decay becomes one decay per key channel), fp32:
+ *   GDN_RECORD_CHANNEL (a reading of Kimi-K3 KDA, which [vLLM] Purpose names
+ *     as a user of the same protocol without giving its arithmetic: the
+ *     scalar decay becomes one decay per key channel), fp32:
  *     delta[T][V] | k_hat[T][K] | alpha[T][K]; it goes with gate_mode
  *     GDN_GATE_CHANNEL and the commit replays
  *     h[v][k] = fma(delta_t[v], k_hat_t[k], h[v][k] * alpha_t[k]).

@@ -12,8 +12,8 @@ shared library and marshals numpy arrays:
   independent heads (the plain definition: every state kept).
 * :func:`replay_heads` -- replay of recorded tokens (the commit update).
 * :func:`native_heads_ch`, :func:`replay_heads_ch` -- the same with one decay
-  per key channel (the KDA reading: the pages name Kimi-K3 KDA as a user of
-  the same protocol but print none of its arithmetic).
+  per key channel (a reading of Kimi-K3 KDA, which the vLLM RecoverSSM PR's
+  Purpose names as a user of the same protocol without its arithmetic).
 * :func:`align_plan` -- align-mode source / final / boundary slots, by walking
   token positions.
 * :func:`bf16_to_f32`, :func:`f32_to_bf16_rne` -- exact widening and

@@ -112,10 +112,10 @@ static void GLUE(replay_head_, SUFFIX)(
 
 
 /*
- * The per-key-channel decay variant (the KDA reading: the pages name Kimi-K3
- * KDA as a user of the same record-and-replay protocol but give none of its
- * arithmetic; the reading taken is the gated delta rule with the scalar decay
- * replaced by one decay per key channel). For token t the log-decay is a
+ * The per-key-channel decay variant (a reading of Kimi-K3 KDA: [vLLM] Purpose
+ * names it as a user of the same record-and-replay protocol but the pages give
+ * none of its arithmetic; the reading taken is the gated delta rule with the
+ * scalar decay replaced by one decay per key channel). For token t the log-decay is a
  * K-vector a_t and alpha_t[k] = exp(a_t[k]); then
  *   h'[v][k] = h[v][k] * alpha_t[k]      (rounded; the value replay uses)
  *   u, delta, the update and o as in native_head above,

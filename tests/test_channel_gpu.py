@@ -1,8 +1,8 @@
-"""GPU parity of the per-key-channel decay variant (the KDA reading: the pages
-name Kimi-K3 KDA as a user of the same record-and-replay protocol without its
-arithmetic; here the scalar decay becomes one decay per key channel, the
-record keeps alpha[K], and the commit replays
-h[v][k] = fma(delta[v], k_hat[k], h[v][k] * alpha[k])).
+"""GPU parity of the per-key-channel decay variant (a reading of Kimi-K3 KDA,
+which the vLLM RecoverSSM PR's Purpose names as a user of the same
+record-and-replay protocol without its arithmetic; here the scalar decay
+becomes one decay per key channel, the record keeps alpha[K], and the commit
+replays h[v][k] = fma(delta[v], k_hat[k], h[v][k] * alpha[k])).
 
 Bars as the other parity tests: outputs, records and committed states within
 the normwise 1e-5 of the oracle's per-channel rule; the commit bit-exact
