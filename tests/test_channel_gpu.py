@@ -168,3 +168,22 @@ def test_channel_ring_align(gdn):
     for layer in range(spec.layers):
         check_channel_layer(h, a_ch, layer, np.arange(spec.rows), wl.n_accept, pre[layer],
                             bnd=(bl, bs), dst=dst)
+
+
+@pytest.mark.parametrize("seed", [41, 42])
+def test_channel_extreme_decays(gdn, seed):
+    """Channels that never decay (log-decay 0), channels decayed into the fp32
+    subnormal range (-100) and channels wiped (-inf) in the same window."""
+    spec = W.shrink(W.ALL_LAYER, layers=1)
+    wl = W.make_workload(spec, device="cuda", seed=seed)
+    a_ch = W.make_channel_decays(wl, device="cuda")
+    a_ch[..., :16] = 0.0
+    a_ch[..., 16:32] = -100.0
+    a_ch[:, ::3, :, 32:40] = float("-inf")
+    h = Harness(wl, record_kind=G.RECORD_CHANNEL)
+    pre = wl.state.clone()
+    verify_ch(h, a_ch, 0)
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    check_channel_layer(h, a_ch, 0, np.arange(spec.rows), wl.n_accept, pre[0])
