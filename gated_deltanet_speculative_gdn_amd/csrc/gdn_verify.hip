@@ -141,14 +141,16 @@ __device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x,
 // Only the keys and queries are needed whole (the dot products); keeping the
 // row-indexed fields to the owned rows lets more workgroups share a CU at long
 // record capacities.
-// With one decay per key channel (CH) three more [TT][128] arrays follow:
+// With one decay per key channel (CH) more [TT][128] arrays follow:
 //   al  the decays of every position;  kx, qx  the window's keys and queries
 //   scaled channel by channel by the decay products G(0, p+1), the vectors the
 //   checkpoint is contracted with (the scalar G(0, p+1) of the scalar-decay
-//   rule is then 1).
-template <int TT, int RW, bool CH = false> struct Lds {
-    static constexpr size_t kFloats =
-        2 * TT * kDim + 3 * TT * RW + 3 * TT + 2 * TT * TT + (CH ? 3 * TT * kDim : 0);
+//   rule is then 1). Only the native baseline (SNAP) keeps kx, qx apart: it
+//   still needs the keys themselves afterwards; verify scales khat and qt in
+//   place once the coefficients are formed.
+template <int TT, int RW, bool CH = false, bool SNAP = false> struct Lds {
+    static constexpr size_t kFloats = 2 * TT * kDim + 3 * TT * RW + 3 * TT + 2 * TT * TT +
+                                      (CH ? (SNAP ? 3 : 1) * TT * kDim : 0);
     float *khat, *qt, *vd, *dw, *ob, *g, *be, *g0, *ca, *cb, *al, *kx, *qx;
     __device__ explicit Lds(float* base)
         : khat(base), qt(base + TT * kDim), vd(base + 2 * TT * kDim), dw(vd + TT * RW),
@@ -169,7 +171,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     constexpr int kChunks = kDim / kRowsPerWg;
     extern __shared__ float lds_raw[];
     const int T = p.T;   // record capacity (record addressing); T <= TT
-    const Lds<TT, kRowsPerWg, CH> L(lds_raw);
+    const Lds<TT, kRowsPerWg, CH, SNAP> L(lds_raw);
 
     const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int chunk = (int)(item % kChunks);
@@ -456,7 +458,12 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     }
     if constexpr (CH) {
         // the vectors the checkpoint meets: k_p and q_p scaled channel by
-        // channel by the decays of positions 0 .. p, in that order
+        // channel by the decays of positions 0 .. p, in that order (verify
+        // overwrites the staged keys and queries once every coefficient job
+        // has read them)
+        if constexpr (!SNAP) __syncthreads();
+        float* const kdst = SNAP ? L.kx : L.khat;
+        float* const qdst = SNAP ? L.qx : L.qt;
         for (int i = tid; i < w * (kDim / 4); i += NT) {
             const int pp = j0 + i / (kDim / 4);
             const int c = 4 * (i % (kDim / 4));
@@ -469,8 +476,8 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
                     for (int e = 0; e < 4; ++e) gam[e] = gam[e] * x[e];
                 }
             const f32x4 kv = ld4(L.khat + pp * kDim + c), qv = ld4(L.qt + pp * kDim + c);
-            st4(L.kx + pp * kDim + c, f32x4{gam.x * kv.x, gam.y * kv.y, gam.z * kv.z, gam.w * kv.w});
-            st4(L.qx + pp * kDim + c, f32x4{gam.x * qv.x, gam.y * qv.y, gam.z * qv.z, gam.w * qv.w});
+            st4(kdst + pp * kDim + c, f32x4{gam.x * kv.x, gam.y * kv.y, gam.z * kv.z, gam.w * kv.w});
+            st4(qdst + pp * kDim + c, f32x4{gam.x * qv.x, gam.y * qv.y, gam.z * qv.z, gam.w * qv.w});
         }
         for (int t = tid; t < w; t += NT) L.g0[j0 + t] = 1.f;
     } else {
@@ -498,7 +505,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         if (pp >= P) break;
         const float g0 = L.g0[pp];
         float pk[R];
-        tile_dot<R>(h, (CH ? L.kx : L.khat) + pp * kDim, lane8, pk);
+        tile_dot<R>(h, (CH && SNAP ? L.kx : L.khat) + pp * kDim, lane8, pk);
         float u[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) u[r] = g0 * pk[r];
@@ -515,7 +522,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int r = 0; r < R; ++r) L.dw[pp * kRowsPerWg + rl + r] = dreg[pp][r];  // same value in all 8 lanes
 
         float pq[R];
-        tile_dot<R>(h, (CH ? L.qx : L.qt) + pp * kDim, lane8, pq);
+        tile_dot<R>(h, (CH && SNAP ? L.qx : L.qt) + pp * kDim, lane8, pq);
         float o[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = g0 * pq[r];
@@ -580,7 +587,7 @@ hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
-    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R, CH>::kFloats;
+    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R, CH, SNAP>::kFloats;
     const size_t lds = need > (size_t)p.lds_floor ? need : (size_t)p.lds_floor;
     return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT, CH>),
                            dim3(grid), dim3(NT), kargs, lds, s);
