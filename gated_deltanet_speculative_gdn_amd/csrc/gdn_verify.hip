@@ -161,7 +161,8 @@ template <int TT, int RW, bool CH = false, bool SNAP = false> struct Lds {
 // NT threads per workgroup, R rows of the head per thread: a workgroup covers
 // NT/8 * R rows, so a head is split over kChunks workgroups. Each stages the
 // whole window (the norms and dot products need all 128 columns); the
-// head-level record fields (key, gate) are written by the first chunk.
+// head-level record fields (key, gate or per-channel decays) are written by
+// the first chunk.
 template <typename StateT, bool SNAP, int R, int NT, int TT, bool CH>
 __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 {
