@@ -187,3 +187,35 @@ def test_channel_extreme_decays(gdn, seed):
     torch.cuda.synchronize()
     assert h.err_value() == 0
     check_channel_layer(h, a_ch, 0, np.arange(spec.rows), wl.n_accept, pre[0])
+
+
+def test_channel_records_with_conv_compaction(gdn):
+    """The fused launch with per-channel decay records: the state replay equals
+    a plain commit of the same records bit for bit, and the conv states equal
+    the oracle's token walk."""
+    from test_conv_commit_gpu import expected_pool, raw
+    spec = W.shrink(W.ALL_LAYER, layers=2)
+    wl = W.make_workload(spec, device="cuda", seed=131)
+    a_ch = W.make_channel_decays(wl, device="cuda")
+    cv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda")
+    h = Harness(wl, record_kind=G.RECORD_CHANNEL)
+    for layer in range(spec.layers):
+        verify_ch(h, a_ch, layer)
+    torch.cuda.synchronize()
+    ref_state = wl.state.clone()
+    ref_pools = G.Pools(ref_state, h.rec, spec.hk, spec.rec_tokens, G.RECORD_CHANNEL)
+    G.gdn_commit_all_layers(ref_pools, h.state_slot, h.state_slot, h.rec_slot, h.n_accept,
+                            err_flags=h.err)
+    pre = raw(cv.state)
+    x = raw(cv.x)
+    G.gdn_commit_all_layers_conv(h.pools, G.ConvPools(cv.state, cv.x), h.state_slot,
+                                 h.state_slot, h.rec_slot, h.n_accept,
+                                 conv_tok_start=h.tok_start, err_flags=h.err)
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    assert torch.equal(pool_bits(wl.state), pool_bits(ref_state)), "state replay differs"
+    got = raw(cv.state)
+    for layer in range(spec.layers):
+        exp = expected_pool(pre[layer], x[layer], range(spec.rows), wl.state_slot, wl.state_slot,
+                            wl.n_accept, wl.tok_start)
+        np.testing.assert_array_equal(got[layer], exp, err_msg=f"layer {layer}")
