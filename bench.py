@@ -279,15 +279,20 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def counters_traffic(commit_launch_bytes):
+def counters_traffic(workload, commit_launch_bytes, path=COUNTERS_FILE):
     """HBM bytes per commit launch from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when it is absent, was taken on a different kernel
+    source, or on another workload or configuration (told apart by the
+    workload name and the launch's algorithmic bytes, which differ with the
+    state dtype, the record kind, the conv states and the accepted counts)."""
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != source_hash() or not c.get("bytes_per_launch"):
+    if (c.get("kernel_source_hash") != source_hash() or c.get("workload") != workload
+            or c.get("algorithmic_bytes_per_launch") != int(commit_launch_bytes)
+            or not c.get("bytes_per_launch")):
         return None
     return int(c["bytes_per_launch"])
 
@@ -310,6 +315,10 @@ def main():
     ap.add_argument("--conv", action="store_true",
                     help="also compact bf16 short-conv states (width-4 conv over the mixed "
                          "q/k/v channels) in the commit launch")
+    ap.add_argument("--accepted", default="uniform", choices=["uniform", "rates"],
+                    help="uniform: accepted counts as the workload draws them; rates: drawn "
+                         "from per-position draft acceptance rates (.856/.694/.558 for the "
+                         "three drafts of a 4-token window)")
     ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
@@ -325,6 +334,9 @@ def main():
     if spec.ring_steps and (args.record == "payload" or args.conv):
         print("the ring workload needs correction records and no conv states", file=sys.stderr)
         sys.exit(2)
+    if spec.ring_steps and args.accepted == "rates":
+        print("the ring workload's flush commits every ring record", file=sys.stderr)
+        sys.exit(2)
     if args.gating == "channel" and args.record == "payload":
         print("per-channel decays keep their own record kind, not the payload record",
               file=sys.stderr)
@@ -334,6 +346,8 @@ def main():
     dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
     log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
     wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    if args.accepted == "rates":
+        W.draw_acceptance_rate_counts(wl)
     conv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if args.conv else None
     payload = args.record == "payload"
     channel = args.gating == "channel"
@@ -382,7 +396,7 @@ def main():
     com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
     ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
     step_gbs = (launches * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
-    traffic = counters_traffic(acc["commit_bytes_per_launch"])
+    traffic = counters_traffic(spec.name, acc["commit_bytes_per_launch"])
     # the dominant kernel of the step: the one with the larger share of its time
     if com_ms >= graph_ms:
         roofline = {"bound": "hbm", "kernel": "commit_all_layers", "achieved": com_gbs,
@@ -411,7 +425,9 @@ def main():
                    "head_dim": 128, "verify_tokens": spec.window, "state_dtype": args.state_dtype,
                    "gating": args.gating, "out_dtype": args.out_dtype, "conv_states": args.conv,
                    "record": "channel" if channel else args.record, "ring_steps": spec.ring_steps, "block": spec.block,
-                   "accepted": f"U{{{spec.n_lo}..{spec.n_hi}}}"},
+                   "accepted": (f"U{{{spec.n_lo}..{spec.n_hi}}}" if args.accepted == "uniform" else
+                                "rates " + "/".join(f"{r:g}" for r in
+                                                    W.MTP_ACCEPTANCE_RATES[: spec.window - 1]))},
         "roofline": roofline,
         "kernels": {
             "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": launches,

@@ -291,8 +291,14 @@ def make_conv(wl: Workload, state_len: int = 3, dtype=torch.bfloat16, device="cp
     return ConvInputs(state, x)
 
 
+# Per-position draft acceptance for MTP with five draft tokens, as quoted in the
+# review thread of the vLLM RecoverSSM PR (position i accepted, given 0..i-1 were).
+MTP_ACCEPTANCE_RATES = (0.856, 0.694, 0.558, 0.457, 0.376)
+ACCEPT_SEED_OFFSET = 7919
+
+
 def acceptance_rate_counts(rng: np.random.Generator, rows: int,
-                           rates=(0.856, 0.694, 0.558, 0.457, 0.376)) -> np.ndarray:
+                           rates=MTP_ACCEPTANCE_RATES) -> np.ndarray:
     """Accepted counts drawn from per-position acceptance rates (a draft token
     at position i is accepted with probability rates[i], given the ones before
     it were), the bonus token always committed. The default rates are the
@@ -308,3 +314,19 @@ def acceptance_rate_counts(rng: np.random.Generator, rows: int,
         alive &= acc
         n += alive
     return n
+
+
+def draw_acceptance_rate_counts(wl: Workload, seed: int | None = None) -> None:
+    """Replace the accepted counts of the workload's real rows (in place) by
+    counts drawn from the per-position acceptance rates of its draft tokens
+    (window - 1 drafts and the bonus token, so n in 1 .. window); padding rows
+    keep n = 0. Not defined for the replay ring, whose flush commits every
+    ring record."""
+    s = wl.spec
+    if s.ring_steps:
+        raise ValueError("the replay ring commits all of its records at the flush")
+    if s.window - 1 > len(MTP_ACCEPTANCE_RATES):
+        raise ValueError(f"acceptance rates are given for {len(MTP_ACCEPTANCE_RATES)} drafts")
+    rng = np.random.default_rng((s.seed if seed is None else seed) + ACCEPT_SEED_OFFSET)
+    real = np.flatnonzero(wl.win_len > 0)
+    wl.n_accept[real] = acceptance_rate_counts(rng, len(real), MTP_ACCEPTANCE_RATES[: s.window - 1])

@@ -57,3 +57,26 @@ def test_acceptance_rate_counts():
     n = W.acceptance_rate_counts(rng, 200000, rates=(0.856, 0.694, 0.558))
     assert n.min() >= 1 and n.max() <= 4
     assert abs((n >= 2).mean() - 0.856) < 0.01 and abs((n >= 4).mean() - 0.558) < 0.01
+
+
+def test_draw_acceptance_rate_counts_on_the_bench_workload():
+    """Real rows get n in 1..D from the first D-1 rates; padding rows keep 0; the
+    ring workload is refused (its flush commits every record)."""
+    wl = W.make_workload(W.WORKLOADS["tiny_l1_b1_h1"])
+    W.draw_acceptance_rate_counts(wl)
+    assert 1 <= wl.n_accept[0] <= wl.spec.window
+    spec = W.MTP_B64
+    import dataclasses
+    small = dataclasses.replace(spec, layers=1)
+    wl = W.make_workload(small)
+    W.draw_acceptance_rate_counts(wl)
+    real = wl.win_len > 0
+    assert (wl.n_accept[~real] == 0).all()
+    assert wl.n_accept[real].min() >= 1 and wl.n_accept[real].max() <= spec.window
+    again = W.make_workload(small)
+    W.draw_acceptance_rate_counts(again)
+    assert (again.n_accept == wl.n_accept).all()       # seeded
+    ring = dataclasses.replace(W.WORKLOADS["ring_align_l36_b256_l16"], layers=1)
+    import pytest
+    with pytest.raises(ValueError):
+        W.draw_acceptance_rate_counts(W.make_workload(ring))
