@@ -34,8 +34,10 @@
 // the pool. Thread t holds head rows row0 + R*(t/8) + r and columns
 // 4*(t%8) + 32*c + e (c, e = 0..3): each 16-byte load of eight neighbouring
 // lanes covers a whole 128-byte row segment, and a length-128 reduction is 16
-// fmas in the lane plus a three-step DPP sum over the eight lanes of a row
-// group. The window's vectors and the per-item scalar coefficients are staged
+// fmas in the lane plus three DPP steps over the eight lanes of a row group,
+// arranged so that lanes 0-3 end with the even rows' sums and lanes 4-7 with
+// the odd rows' (the per-row recurrence then runs in four lanes per row, not
+// eight). The window's vectors and the per-item scalar coefficients are staged
 // in LDS once.
 //
 // Options carried in the parameters: gates formed here from raw projections
@@ -107,25 +109,38 @@ template <int R> struct TileIO<uint16_t, R> {
     }
 };
 
-// Row-group dot product of the tile with one staged 128-vector: R sums, each
-// identical in all eight lanes of the group.
+// Row-group dot product of the tile with one staged 128-vector, the rows'
+// sums split over the group: 16 fmas per row in each lane, then for each pair
+// of rows (2m, 2m+1) one exchange between lane i and lane 7-i of the group, in
+// which lanes 0-3 keep row 2m's partial sums and lanes 4-7 row 2m+1's, and two
+// exchanges inside each half. out[m] is row 2m's sum in lanes 0-3 and row
+// 2m+1's in lanes 4-7 (hi), identical in the four lanes of a half: five
+// instructions a pair where a sum in all eight lanes would take six, and the
+// per-row arithmetic that follows is done by half as many lanes per row.
 template <int R>
-__device__ __forceinline__ void tile_dot(const f32x4 (&h)[R][4], const float* x, int lane8, float (&out)[R])
+__device__ __forceinline__ void tile_dot_split(const f32x4 (&h)[R][4], const float* x, int lane8, bool hi,
+                                               float (&out)[R / 2])
 {
     f32x4 xv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) xv[c] = ld4(x + 4 * lane8 + 32 * c);
+    float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        float acc = 0.f;
+        acc[r] = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(h[r][c][e], xv[c][e], acc);
-        out[r] = acc;
+            for (int e = 0; e < 4; ++e) acc[r] = __builtin_fmaf(h[r][c][e], xv[c][e], acc[r]);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) out[r] = sum8(out[r]);
+    for (int m = 0; m < R / 2; ++m) {
+        const float keep = hi ? acc[2 * m + 1] : acc[2 * m];
+        const float send = hi ? acc[2 * m] : acc[2 * m + 1];
+        float s = keep + dpp<kDppRowHalfMirror>(send);
+        s = s + dpp<kDppQuadXor1>(s);
+        out[m] = s + dpp<kDppQuadXor2>(s);
+    }
 }
 
 // LDS layout of one workgroup (floats), TT = compile-time window capacity
@@ -166,7 +181,7 @@ template <int TT, int RW, bool CH = false, bool SNAP = false> struct Lds {
 template <typename StateT, bool SNAP, int R, int NT, int TT, bool CH>
 __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 {
-    static_assert(R == 1 || R == 2 || R == 4, "rows per thread");
+    static_assert(R == 2 || R == 4, "rows per thread: pairs of rows");
     constexpr int kRowsPerWg = NT / 8 * R;
     static_assert(kDim % kRowsPerWg == 0, "workgroup rows divide the head");
     constexpr int kChunks = kDim / kRowsPerWg;
@@ -494,47 +509,51 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
 
     // ---- the window, position by position (unrolled over the capacity TT;
     // the corrections of the owned rows stay in registers) ----
-    const int rl = R * grp;           // first owned row of the group, relative to row0
-    float dreg[TT][R];
+    // Each lane finishes rows rm, rm + 2, ... (RH of them): lanes 0-3 of the
+    // group the even rows of the group's R, lanes 4-7 the odd ones.
+    constexpr int RH = R / 2;
+    const bool hi = (lane8 & 4) != 0;
+    const int rm = R * grp + (hi ? 1 : 0);   // relative to row0
+    float dreg[TT][RH];
 #pragma unroll
     for (int pp = 0; pp < TT; ++pp) {
         if (pp < j0) {                 // ring position: its recorded correction
 #pragma unroll
-            for (int r = 0; r < R; ++r) dreg[pp][r] = L.vd[pp * kRowsPerWg + rl + r];
+            for (int m = 0; m < RH; ++m) dreg[pp][m] = L.vd[pp * kRowsPerWg + rm + 2 * m];
             continue;
         }
         if (pp >= P) break;
         const float g0 = L.g0[pp];
-        float pk[R];
-        tile_dot<R>(h, (CH && SNAP ? L.kx : L.khat) + pp * kDim, lane8, pk);
-        float u[R];
+        float pk[RH];
+        tile_dot_split<R>(h, (CH && SNAP ? L.kx : L.khat) + pp * kDim, lane8, hi, pk);
+        float u[RH];
 #pragma unroll
-        for (int r = 0; r < R; ++r) u[r] = g0 * pk[r];
+        for (int m = 0; m < RH; ++m) u[m] = g0 * pk[m];
 #pragma unroll
         for (int j = 0; j < pp; ++j) {
             const float cf = L.ca[j * TT + pp];
 #pragma unroll
-            for (int r = 0; r < R; ++r) u[r] = __builtin_fmaf(cf, dreg[j][r], u[r]);
+            for (int m = 0; m < RH; ++m) u[m] = __builtin_fmaf(cf, dreg[j][m], u[m]);
         }
         const float be = L.be[pp];
 #pragma unroll
-        for (int r = 0; r < R; ++r) dreg[pp][r] = be * (L.vd[pp * kRowsPerWg + rl + r] - u[r]);
+        for (int m = 0; m < RH; ++m) dreg[pp][m] = be * (L.vd[pp * kRowsPerWg + rm + 2 * m] - u[m]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) L.dw[pp * kRowsPerWg + rl + r] = dreg[pp][r];  // same value in all 8 lanes
+        for (int m = 0; m < RH; ++m) L.dw[pp * kRowsPerWg + rm + 2 * m] = dreg[pp][m];  // same value in 4 lanes
 
-        float pq[R];
-        tile_dot<R>(h, (CH && SNAP ? L.qx : L.qt) + pp * kDim, lane8, pq);
-        float o[R];
+        float pq[RH];
+        tile_dot_split<R>(h, (CH && SNAP ? L.qx : L.qt) + pp * kDim, lane8, hi, pq);
+        float o[RH];
 #pragma unroll
-        for (int r = 0; r < R; ++r) o[r] = g0 * pq[r];
+        for (int m = 0; m < RH; ++m) o[m] = g0 * pq[m];
 #pragma unroll
         for (int j = 0; j <= pp; ++j) {
             const float cf = L.cb[j * TT + pp];
 #pragma unroll
-            for (int r = 0; r < R; ++r) o[r] = __builtin_fmaf(cf, dreg[j][r], o[r]);
+            for (int m = 0; m < RH; ++m) o[m] = __builtin_fmaf(cf, dreg[j][m], o[m]);
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) L.ob[pp * kRowsPerWg + rl + r] = o[r];   // same value in all 8 lanes
+        for (int m = 0; m < RH; ++m) L.ob[pp * kRowsPerWg + rm + 2 * m] = o[m];   // same value in 4 lanes
     }
     __syncthreads();
 
@@ -567,9 +586,16 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
                 kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
                 dc[c] = CH ? ld4(L.al + t * kDim + 4 * lane8 + 32 * c) : f32x4{g, g, g, g};
             }
+            float dr[R];              // both rows of each pair, from the two halves
+#pragma unroll
+            for (int m = 0; m < RH; ++m) {
+                const float other = dpp<kDppRowHalfMirror>(dreg[t][m]);
+                dr[2 * m] = hi ? other : dreg[t][m];
+                dr[2 * m + 1] = hi ? dreg[t][m] : other;
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const float d = dreg[t][r];
+                const float d = dr[r];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
