@@ -37,22 +37,24 @@ REC_TOKEN_BYTES = (128 + 128 + 1) * 4           # correction, key, gate (fp32)
 PAYLOAD_TOKEN_BYTES = (128 + 128) * 2 + 2 * 4    # raw key, raw value (bf16), gate, beta (fp32)
 CHANNEL_TOKEN_BYTES = (128 + 128 + 128) * 4      # correction, key, per-channel decays (fp32)
 CHANNEL_GATE_BYTES = 128 * 4 + 4                 # per-channel log-decays and beta, per head
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "commit_counters.json")
-KERNEL_SOURCES = ["gated_deltanet_speculative_gdn_amd/csrc/gdn_commit.hip",
-                  "gated_deltanet_speculative_gdn_amd/csrc/gdn_device.hpp",
-                  "gated_deltanet_speculative_gdn_amd/csrc/gdn_kernels.hpp"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+_CSRC = "gated_deltanet_speculative_gdn_amd/csrc/"
+KERNEL_SOURCES = {
+    "commit_all_layers": [_CSRC + "gdn_commit.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp"],
+    "verify": [_CSRC + "gdn_verify.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    """Hash of the commit kernel's sources with comments and blank space
-    removed, so that the stored counters stay valid across comment edits."""
+def source_hash(kernel: str = "commit_all_layers") -> str:
+    """Hash of one kernel's sources with comments and blank space removed, so
+    that the stored counters stay valid across comment edits."""
     import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -279,22 +281,26 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def counters_traffic(workload, commit_launch_bytes, path=COUNTERS_FILE):
-    """HBM bytes per commit launch from the committed rocprofv3 counter
-    summary, or None when it is absent, was taken on a different kernel
-    source, or on another workload or configuration (told apart by the
-    workload name and the launch's algorithmic bytes, which differ with the
-    state dtype, the record kind, the conv states and the accepted counts)."""
+def counters_traffic(kernel, workload, launch_bytes, path=COUNTERS_FILE):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summaries (a list of entries), or None when no entry was taken on this
+    kernel's current source, this workload and this configuration (told apart
+    by the launch's algorithmic bytes, which differ with the state dtype, the
+    record kind, the conv states and the accepted counts)."""
     try:
         with open(path) as f:
-            c = json.load(f)
+            entries = json.load(f)
     except (OSError, ValueError):
         return None
-    if (c.get("kernel_source_hash") != source_hash() or c.get("workload") != workload
-            or c.get("algorithmic_bytes_per_launch") != int(commit_launch_bytes)
-            or not c.get("bytes_per_launch")):
+    if not isinstance(entries, list):
         return None
-    return int(c["bytes_per_launch"])
+    for c in entries:
+        if (isinstance(c, dict) and c.get("kernel") == kernel and c.get("workload") == workload
+                and c.get("kernel_source_hash") == source_hash(kernel)
+                and c.get("algorithmic_bytes_per_launch") == int(launch_bytes)
+                and c.get("bytes_per_launch")):
+            return int(c["bytes_per_launch"])
+    return None
 
 
 def main():
@@ -396,16 +402,17 @@ def main():
     com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
     ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
     step_gbs = (launches * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
-    traffic = counters_traffic(spec.name, acc["commit_bytes_per_launch"])
+    com_traffic = counters_traffic("commit_all_layers", spec.name, acc["commit_bytes_per_launch"])
+    ver_traffic = counters_traffic("verify", spec.name, acc["verify_bytes_per_launch"])
     # the dominant kernel of the step: the one with the larger share of its time
     if com_ms >= graph_ms:
         roofline = {"bound": "hbm", "kernel": "commit_all_layers", "achieved": com_gbs,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": com_gbs / HBM_PEAK_GBS,
-                    "traffic": traffic}
+                    "traffic": com_traffic}
     else:
         roofline = {"bound": "hbm", "kernel": "verify", "achieved": ver_gbs,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ver_gbs / HBM_PEAK_GBS,
-                    "traffic": None}
+                    "traffic": ver_traffic}
 
     result = {
         "metric": "commit+verify state-updates/s and achieved HBM GB/s (% peak), B=64 D=4 48 layers",
@@ -433,14 +440,16 @@ def main():
             "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": launches,
                        "eager_us_per_launch": ver_eager_us,
                        "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
+                       "counter_bytes_per_launch": ver_traffic,
                        "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
             "commit_all_layers": {"us_per_launch": com_ms * 1e3, "launches_per_step": 1,
                                   "algorithmic_bytes_per_launch": acc["commit_bytes_per_launch"],
+                                  "counter_bytes_per_launch": com_traffic,
                                   "GB/s": com_gbs, "frac_of_peak": com_gbs / HBM_PEAK_GBS},
         },
         "step_GB/s": step_gbs,
         "updates_per_step": {"verify": acc["verify_updates"], "commit": acc["commit_updates"]},
-        "kernel_source_hash": source_hash(),
+        "kernel_source_hash": {k: source_hash(k) for k in KERNEL_SOURCES},
     }
 
     if args.copy_probe_mib:
