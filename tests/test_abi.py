@@ -300,3 +300,38 @@ def test_check_slots_rejects_bad_arguments(lib):
     assert lib.gdn_check_slots(4, fake, fake, None, fake, None, None, None, None) == E_NULL
     assert lib.gdn_check_slots(4, fake, fake, None, fake, fake, None, fake, None) == E_NULL
     assert lib.gdn_check_slots(0, fake, fake, None, fake, None, None, fake, None) == OK
+
+
+def test_headers_are_plain_c_and_link_against_the_library(tmp_path, lib):
+    """The public headers compile as strict C99 (no C++ or HIP headers needed),
+    every declared function can be referenced from C, and a C program linked
+    against the library gets the documented results of calls that need no GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = declared_functions()
+    src = tmp_path / "abi.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"gdn_replay.h\"\n#include \"gdn_probe.h\"\n"
+        "int main(void) {\n"
+        "    typedef void (*fn_t)(void);\n"
+        "    const fn_t fns[] = {" + ", ".join(f"(fn_t)&{n}" for n in names) + "};\n"
+        "    unsigned i;\n"
+        "    for (i = 0; i < sizeof fns / sizeof fns[0]; ++i) if (!fns[i]) return 10;\n"
+        f"    if (gdn_abi_version() != {lib.gdn_abi_version()}) return 11;\n"
+        "    if (gdn_verify(NULL, 0, 1, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) != GDN_ERR_NULL) return 12;\n"
+        "    if (gdn_commit_all_layers(NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) != GDN_ERR_NULL) return 13;\n"
+        "    printf(\"%s\\n\", gdn_status_string(GDN_ERR_ALIGN));\n"
+        "    return 0;\n}\n")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(B.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+           str(src), "-o", str(exe), "-L", libdir, "-lgdnreplay", f"-Wl,-rpath,{libdir}",
+           "-Wl,--allow-shlib-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.startswith("a pointer or stride")
