@@ -129,12 +129,39 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _i32(t: torch.Tensor | None, name: str):
+# Argument checks. The C ABI sees only pointers and strides, so the sizes it
+# cannot see are checked here, where the tensors' shapes are known: every
+# buffer a kernel will address must be a device tensor large enough for the
+# rows, heads and tokens of the call. Shape checks come before the device
+# check, so that they can be exercised without a GPU.
+
+def _on_device(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor (the kernels address it on the GPU)")
+    return t
+
+
+def _i32(t: torch.Tensor | None, name: str, n: int | None = None):
+    """A contiguous int32 device tensor; with n, 1-D with at least n entries."""
     if t is None:
         return None
-    if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda:
+    if t.dtype != torch.int32 or not t.is_contiguous():
         raise TypeError(f"{name} must be a contiguous int32 device tensor")
-    return t
+    if n is not None and (t.dim() != 1 or t.shape[0] < n):
+        raise TypeError(f"{name} must be a 1-D int32 tensor with at least {n} entries")
+    return _on_device(t, name)
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 1:
+        raise TypeError(f"{name} must be a 1-D int32 tensor (one entry per row)")
+    return int(t.shape[0])
+
+
+def _flags(t):
+    if t is not None and t.numel() < 1:
+        raise TypeError("err_flags must hold at least one int32")
+    return _i32(t, "err_flags")
 
 
 class Pools:
@@ -149,7 +176,11 @@ class Pools:
                  record_kind: int = RECORD_CORRECTION):
         self.state = list(state) if not torch.is_tensor(state) else [state[i] for i in range(state.shape[0])]
         self.rec = list(rec) if not torch.is_tensor(rec) else [rec[i] for i in range(rec.shape[0])]
+        if not 1 <= len(self.state) <= GDN_MAX_LAYERS or len(self.rec) != len(self.state):
+            raise TypeError(f"1..{GDN_MAX_LAYERS} layers, one state and one record pool per layer")
         s0 = self.state[0]
+        if s0.dim() != 4:
+            raise TypeError("state pools are [slots][HV][V][K]")
         self.num_layers = len(self.state)
         self.num_slots, self.hv, V, K = s0.shape
         self.hk = num_k_heads
@@ -157,7 +188,15 @@ class Pools:
         self.dtype = s0.dtype
         if self.dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("state pools are fp32 or bf16")
-        self.num_rec_slots = self.rec[0].shape[0]
+        stride = rec_stride(rec_tokens, record_kind)
+        r0 = self.rec[0]
+        if r0.dtype != torch.float32 or r0.dim() != 3 or r0.shape[1] != self.hv or r0.shape[2] != stride:
+            raise TypeError(f"record pools are fp32 [rec_slots][HV][{stride}] for {rec_tokens} "
+                            "tokens of this record kind")
+        for s_, r_ in zip(self.state, self.rec):
+            if s_.shape != s0.shape or s_.dtype != s0.dtype or r_.shape != r0.shape or r_.dtype != r0.dtype:
+                raise TypeError("every layer's pools have the same shape and dtype")
+        self.num_rec_slots = r0.shape[0]
         st = gdn_pools()
         st.num_layers = self.num_layers
         st.num_v_heads = self.hv
@@ -173,6 +212,8 @@ class Pools:
         for i, (s, r) in enumerate(zip(self.state, self.rec)):
             if not (s.is_contiguous() and r.is_contiguous()):
                 raise TypeError("pools must be contiguous")
+            _on_device(s, "state pool")
+            _on_device(r, "record pool")
             st.state[i] = s.data_ptr()
             st.rec[i] = r.data_ptr()
         self.c = st
@@ -192,7 +233,11 @@ class ConvPools:
     def __init__(self, state, x):
         self.state = list(state) if not torch.is_tensor(state) else [state[i] for i in range(state.shape[0])]
         self.x = list(x) if not torch.is_tensor(x) else [x[i] for i in range(x.shape[0])]
+        if not 1 <= len(self.state) <= GDN_MAX_LAYERS or len(self.x) != len(self.state):
+            raise TypeError(f"1..{GDN_MAX_LAYERS} layers, one conv state pool and one input per layer")
         s0, x0 = self.state[0], self.x[0]
+        if s0.dim() != 3:
+            raise TypeError("conv state pools are [slots][state_len][C]")
         self.num_slots, self.state_len, self.channels = s0.shape
         self.dtype = s0.dtype
         if self.dtype not in (torch.float32, torch.bfloat16) or x0.dtype != self.dtype:
@@ -208,19 +253,25 @@ class ConvPools:
         st.x_tok_stride = x0.stride(0)
         st.num_tokens = x0.shape[0]
         for i, (s_, x_) in enumerate(zip(self.state, self.x)):
-            if not s_.is_contiguous() or x_.stride() != x0.stride() or x_.shape != x0.shape:
-                raise TypeError("conv pools contiguous, conv inputs of one shape and stride")
+            if not s_.is_contiguous() or x_.stride() != x0.stride() or x_.shape != x0.shape \
+                    or s_.shape != s0.shape or s_.dtype != s0.dtype or x_.dtype != x0.dtype:
+                raise TypeError("conv pools contiguous and of one shape, conv inputs of one shape and stride")
+            _on_device(s_, "conv state pool")
+            _on_device(x_, "conv input")
             st.state[i] = s_.data_ptr()
             st.x[i] = x_.data_ptr()
         self.c = st
 
 
-def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
+def _io(pools, q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     """a [tokens][HV] (log-gate, or raw projection with A_log / dt_bias) or
     a [tokens][HV][128] (one log-decay per key channel); b [tokens][HV]."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+    hk, hv = pools.hk, pools.hv
+    for name, t, heads in (("q", q, hk), ("k", k, hk), ("v", v, hv)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or t.shape[2] != GDN_HEAD_DIM:
             raise TypeError(f"{name} must be a bf16 [tokens][heads][128] view, feature-contiguous")
+        if t.shape[1] < heads:
+            raise TypeError(f"{name} has {t.shape[1]} heads, the pools {heads}")
     channel = a.dim() == 3
     if channel:
         if a.dtype != torch.float32 or a.stride(2) != 1 or a.stride(1) != a.shape[2] \
@@ -230,10 +281,15 @@ def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     elif a.dtype != torch.float32 or b.dtype != torch.float32 or a.dim() != 2 \
             or a.stride(1) != 1 or b.stride() != a.stride():
         raise TypeError("a and b must be fp32 [tokens][HV] with the same strides")
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.dim() != 3 or out.stride(2) != 1:
+    if (channel and a.shape[2] != GDN_HEAD_DIM) or a.shape[1] < hv or b.shape[1] < hv:
+        raise TypeError(f"a and b must cover the pools' {hv} value heads (and 128 channels)")
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.dim() != 3 or out.stride(2) != 1 \
+            or out.shape[2] != GDN_HEAD_DIM or out.shape[1] < hv:
         raise TypeError("out must be an fp32 or bf16 [tokens][HV][128] view, feature-contiguous")
     if (A_log is None) != (dt_bias is None):
         raise TypeError("raw gates need both A_log and dt_bias")
+    for name, t in (("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("out", out)):
+        _on_device(t, name)
     io = gdn_verify_io()
     io.q, io.q_tok_stride, io.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
     io.k, io.k_tok_stride, io.k_head_stride = k.data_ptr(), k.stride(0), k.stride(1)
@@ -241,7 +297,7 @@ def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
     io.a, io.b, io.gate_tok_stride = a.data_ptr(), b.data_ptr(), b.stride(0)
     io.out, io.out_tok_stride, io.out_head_stride = out.data_ptr(), out.stride(0), out.stride(1)
     io.out_dtype = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
-    io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a.shape[0], out.shape[0])
+    io.num_tokens = min(q.shape[0], k.shape[0], v.shape[0], a.shape[0], b.shape[0], out.shape[0])
     io.scale = float(scale)
     io.gate_mode = GATE_LOG
     if channel:
@@ -251,8 +307,9 @@ def _io(q, k, v, a, b, out, scale, A_log=None, dt_bias=None) -> gdn_verify_io:
         io.decay_tok_stride = a.stride(0)
     if A_log is not None:
         for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
-            if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+            if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous() or t.shape[0] < hv:
                 raise TypeError(f"{name} must be a contiguous fp32 [HV] tensor")
+            _on_device(t, name)
         io.gate_mode = GATE_RAW
         io.A_log, io.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
     return io
@@ -265,38 +322,45 @@ def gdn_verify(pools: Pools, layer: int, state_slot, rec_slot, tok_start, win_le
     A_log and dt_bias given, the raw gate projections (gates formed in the
     kernel). out may be fp32 or bf16."""
     lib = load_library()
-    io = _io(q, k, v, a, b, out, scale, A_log, dt_bias)
-    n = state_slot.shape[0]
-    return _check(lib.gdn_verify(C.byref(pools.c), layer, n, _ptr(_i32(state_slot, "state_slot")),
-                                 _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(tok_start, "tok_start")),
-                                 _ptr(_i32(win_len, "win_len")), _ptr(_i32(rec_base, "rec_base")),
-                                 C.byref(io), _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+    n = _rows(state_slot, "state_slot")
+    args = [_i32(state_slot, "state_slot", n), _i32(rec_slot, "rec_slot", n),
+            _i32(tok_start, "tok_start", n), _i32(win_len, "win_len", n),
+            _i32(rec_base, "rec_base", n)]
+    io = _io(pools, q, k, v, a, b, out, scale, A_log, dt_bias)
+    return _check(lib.gdn_verify(C.byref(pools.c), layer, n, *map(_ptr, args), C.byref(io),
+                                 _ptr(_flags(err_flags)), _stream(stream)))
 
 
 def gdn_native_window(pools: Pools, layer: int, state_slot, tok_start, win_len,
                       q, k, v, a, b, out, snap, *, scale=1.0, A_log=None, dt_bias=None,
                       err_flags=None, stream=None) -> int:
     lib = load_library()
-    io = _io(q, k, v, a, b, out, scale, A_log, dt_bias)
-    if snap.dtype != pools.dtype or not snap.is_contiguous():
-        raise TypeError("snap must be contiguous with the pool's dtype")
-    n = state_slot.shape[0]
-    return _check(lib.gdn_native_window(C.byref(pools.c), layer, n,
-                                        _ptr(_i32(state_slot, "state_slot")),
-                                        _ptr(_i32(tok_start, "tok_start")),
-                                        _ptr(_i32(win_len, "win_len")), C.byref(io), _ptr(snap),
-                                        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+    n = _rows(state_slot, "state_slot")
+    args = [_i32(state_slot, "state_slot", n), _i32(tok_start, "tok_start", n),
+            _i32(win_len, "win_len", n)]
+    io = _io(pools, q, k, v, a, b, out, scale, A_log, dt_bias)
+    _snap(pools, snap, n, "snap")
+    return _check(lib.gdn_native_window(C.byref(pools.c), layer, n, *map(_ptr, args), C.byref(io),
+                                        _ptr(snap), _ptr(_flags(err_flags)), _stream(stream)))
+
+
+def _snap(pools, snap, rows, name):
+    """Snapshots [rows][HV][T][V][K] in the pool's dtype."""
+    need = rows * pools.hv * pools.rec_tokens * GDN_HEAD_DIM * GDN_HEAD_DIM
+    if snap.dtype != pools.dtype or not snap.is_contiguous() or snap.numel() < need:
+        raise TypeError(f"{name} must be contiguous [rows][HV][T][128][128] in the pool's dtype")
+    _on_device(snap, name)
 
 
 def gdn_commit_all_layers(pools: Pools, src_slot, dst_slot, rec_slot, n_accept, bnd_len=None,
                           bnd_slot=None, *, err_flags=None, stream=None) -> int:
     lib = load_library()
-    n = src_slot.shape[0]
-    return _check(lib.gdn_commit_all_layers(
-        C.byref(pools.c), n, _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
-        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
-        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
-        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+    n = _rows(src_slot, "src_slot")
+    args = [_i32(t, name, n) for t, name in ((src_slot, "src_slot"), (dst_slot, "dst_slot"),
+                                             (rec_slot, "rec_slot"), (n_accept, "n_accept"),
+                                             (bnd_len, "bnd_len"), (bnd_slot, "bnd_slot"))]
+    return _check(lib.gdn_commit_all_layers(C.byref(pools.c), n, *map(_ptr, args),
+                                            _ptr(_flags(err_flags)), _stream(stream)))
 
 
 def gdn_commit_all_layers_conv(pools, conv, src_slot, dst_slot, rec_slot, n_accept,
@@ -305,37 +369,45 @@ def gdn_commit_all_layers_conv(pools, conv, src_slot, dst_slot, rec_slot, n_acce
     """The all-layer commit of the state pools (or None) together with the
     short-conv state compaction of ``conv`` (a ConvPools, or None), one launch."""
     lib = load_library()
-    n = src_slot.shape[0]
+    n = _rows(src_slot, "src_slot")
+    args = [_i32(t, name, n) for t, name in ((src_slot, "src_slot"), (dst_slot, "dst_slot"),
+                                             (rec_slot, "rec_slot"), (n_accept, "n_accept"),
+                                             (bnd_len, "bnd_len"), (bnd_slot, "bnd_slot"),
+                                             (conv_tok_start, "conv_tok_start"))]
     return _check(lib.gdn_commit_all_layers_conv(
         C.byref(pools.c) if pools is not None else None,
-        C.byref(conv.c) if conv is not None else None, n,
-        _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
-        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
-        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
-        _ptr(_i32(conv_tok_start, "conv_tok_start")), _ptr(_i32(err_flags, "err_flags")),
-        _stream(stream)))
+        C.byref(conv.c) if conv is not None else None, n, *map(_ptr, args),
+        _ptr(_flags(err_flags)), _stream(stream)))
 
 
 def gdn_native_accept(pools: Pools, snaps, dst_slot, n_accept, *, err_flags=None,
                       stream=None) -> int:
     lib = load_library()
-    arr = (C.c_void_p * len(snaps))(*[s.data_ptr() for s in snaps])
-    return _check(lib.gdn_native_accept(C.byref(pools.c), arr, dst_slot.shape[0],
-                                        _ptr(_i32(dst_slot, "dst_slot")),
-                                        _ptr(_i32(n_accept, "n_accept")),
-                                        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+    n = _rows(dst_slot, "dst_slot")
+    args = [_i32(dst_slot, "dst_slot", n), _i32(n_accept, "n_accept", n)]
+    snaps = list(snaps)
+    if len(snaps) != pools.num_layers:
+        raise TypeError("one snapshot tensor per layer")
+    for s_ in snaps:
+        _snap(pools, s_, n, "snaps[l]")
+    arr = (C.c_void_p * len(snaps))(*[s_.data_ptr() for s_ in snaps])
+    return _check(lib.gdn_native_accept(C.byref(pools.c), arr, n, *map(_ptr, args),
+                                        _ptr(_flags(err_flags)), _stream(stream)))
 
 
 def gdn_align_plan(num_computed, n_accept, block_table, block_size: int, max_accept: int,
                    src_slot, dst_slot, bnd_len, bnd_slot, *, err_flags=None, stream=None) -> int:
     lib = load_library()
+    n = _rows(num_computed, "num_computed")
+    if block_table.dim() != 2 or block_table.shape[0] < n:
+        raise TypeError(f"block_table must be a 2-D int32 tensor with at least {n} rows")
     bt = _i32(block_table, "block_table")
+    args = [_i32(t, name, n) for t, name in ((num_computed, "num_computed"), (n_accept, "n_accept"))]
+    outs = [_i32(t, name, n) for t, name in ((src_slot, "src_slot"), (dst_slot, "dst_slot"),
+                                             (bnd_len, "bnd_len"), (bnd_slot, "bnd_slot"))]
     return _check(lib.gdn_align_plan(
-        num_computed.shape[0], _ptr(_i32(num_computed, "num_computed")),
-        _ptr(_i32(n_accept, "n_accept")), _ptr(bt), bt.stride(0), bt.shape[1], block_size,
-        max_accept, _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
-        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
-        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+        n, _ptr(args[0]), _ptr(args[1]), _ptr(bt), bt.stride(0), bt.shape[1], block_size,
+        max_accept, *map(_ptr, outs), _ptr(_flags(err_flags)), _stream(stream)))
 
 
 def gdn_bandwidth_probe(kind: int, src, dst, nbytes: int | None = None, *, stream=None) -> int:
@@ -344,9 +416,17 @@ def gdn_bandwidth_probe(kind: int, src, dst, nbytes: int | None = None, *, strea
     None for PROBE_WRITE; for PROBE_READ ``dst`` receives one 16-byte word per
     GDN_PROBE_CHUNK bytes."""
     lib = load_library()
+    size = lambda t: 0 if t is None else t.numel() * t.element_size()  # noqa: E731
     if nbytes is None:
-        t = src if src is not None else dst
-        nbytes = t.numel() * t.element_size()
+        nbytes = size(src) if src is not None else size(dst)
+    if kind in (PROBE_READ, PROBE_COPY) and (src is None or not src.is_contiguous() or size(src) < nbytes):
+        raise TypeError(f"src must be a contiguous device tensor of at least {nbytes} bytes")
+    need = nbytes // GDN_PROBE_CHUNK * 16 if kind == PROBE_READ else nbytes
+    if dst is None or not dst.is_contiguous() or size(dst) < need:
+        raise TypeError(f"dst must be a contiguous device tensor of at least {need} bytes")
+    for t, name in ((src, "src"), (dst, "dst")):
+        if t is not None:
+            _on_device(t, name)
     return _check(lib.gdn_bandwidth_probe(kind, _ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
@@ -356,8 +436,9 @@ def gdn_check_slots(src_slot, dst_slot, n_accept, *, rec_slot=None, bnd_len=None
     ``err_flags`` if live rows share a written slot, write another row's
     source or share a record slot."""
     lib = load_library()
-    return _check(lib.gdn_check_slots(
-        src_slot.shape[0], _ptr(_i32(src_slot, "src_slot")), _ptr(_i32(dst_slot, "dst_slot")),
-        _ptr(_i32(rec_slot, "rec_slot")), _ptr(_i32(n_accept, "n_accept")),
-        _ptr(_i32(bnd_len, "bnd_len")), _ptr(_i32(bnd_slot, "bnd_slot")),
-        _ptr(_i32(err_flags, "err_flags")), _stream(stream)))
+    n = _rows(src_slot, "src_slot")
+    args = [_i32(t, name, n) for t, name in ((src_slot, "src_slot"), (dst_slot, "dst_slot"),
+                                             (rec_slot, "rec_slot"), (n_accept, "n_accept"),
+                                             (bnd_len, "bnd_len"), (bnd_slot, "bnd_slot"))]
+    return _check(lib.gdn_check_slots(n, *map(_ptr, args), _ptr(_flags(err_flags)),
+                                      _stream(stream)))
