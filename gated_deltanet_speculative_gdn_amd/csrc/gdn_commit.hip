@@ -11,17 +11,19 @@
 // "feat: add Qwen3.5 GDN ReplaySSM", Summary and Implementation (one replay
 // launch over all layers; a cooperative block of four warps per 128x128 head).
 //
-// One launch over (layer, row, value head, part): a head is split over 2, 4 or
-// 8 workgroups of four wave64s, each owning a contiguous run of its rows. A
-// thread first loads its share of the n records (the workgroup's rows of the
-// corrections, all of the keys, the decays), then its 16-byte pieces of the
-// source head -- thread t owns pieces t + 256*i, so each load instruction of
-// the workgroup covers 4 KiB of contiguous memory. Loads complete in issue
-// order, so the records arrive first; they are staged in LDS, and the replay
-// then runs one piece at a time over all n tokens (elementwise, no
-// reductions), each piece waiting only for its own load. The final state is
-// stored, then in align mode the boundary state kept in a second register
-// tile. State loads and stores are nontemporal (streamed past the caches:
+// One launch over (layer, row, value head, part): a head is split over 8
+// (fp32) or 4 (bf16) workgroups of four wave64s, 8 KiB of state each, each
+// owning a contiguous run of its rows. A thread first loads its share of the
+// n records (the workgroup's rows of the corrections, all of the keys, the
+// decays), then its 16-byte pieces of the source head -- thread t owns pieces
+// t + 256*i, so each load instruction of the workgroup covers 4 KiB of
+// contiguous memory. Loads complete in issue order, so the records arrive
+// first. They are staged in LDS, and the replay (elementwise, no reductions)
+// runs token by token over the thread's pieces: the pieces share their
+// columns, so each token's key and decay are read from LDS once, and the
+// first token's pass waits for each piece's own load in turn, overlapping the
+// transfer of the later pieces. The final state is stored, then in align mode
+// the boundary state kept in a second register tile. State loads and stores are nontemporal (streamed past the caches:
 // nothing here is reused), and the workgroup ids are remapped so that each
 // XCD streams a contiguous range of heads. Because every thread reads all of
 // its source elements before its first store and writes only the elements it
@@ -60,9 +62,13 @@ template <int SPLIT> struct HeadIO<float, SPLIT> {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) st4_nt(head + 4 * piece(part, t, i), h[i]);
     }
-    // row of piece i relative to the workgroup's first row
+    // row of piece i relative to the workgroup's first row: (t / 32) + 8 i
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 5; }
     __device__ static int col0(int t) { return 4 * (t & 31); }
+    // a thread owns kOwnRows rows, one per piece, kGroup rows apart; in the
+    // permuted correction order drow they are contiguous
+    static constexpr int kGroup = kThreads / 32, kOwnRows = kPer;
+    __device__ static int drow(int r) { return (r % kGroup) * kOwnRows + r / kGroup; }
 };
 
 template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
@@ -87,8 +93,11 @@ template <int SPLIT> struct HeadIO<uint16_t, SPLIT> {
             __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(head + 8 * piece(part, t, i)));
         }
     }
+    // row of piece pair i relative to the workgroup's first row: (t / 16) + 16 i
     __device__ static int local_row(int t, int i) { return (t + kThreads * i) >> 4; }
     __device__ static int col0(int t) { return 8 * (t & 15); }
+    static constexpr int kGroup = kThreads / 16, kOwnRows = kPieces;
+    __device__ static int drow(int r) { return (r % kGroup) * kOwnRows + r / kGroup; }
 };
 
 // Row check shared by the state replay and the conv compaction of one launch:
@@ -368,11 +377,19 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
             if (write_bnd) IO::store(pool + bs * slot_elems + head_off, part, t, hb);
         }
     } else {
-    // ---- the n records into LDS ----
+    // ---- the n records into LDS. The corrections of token tt are kept
+    // row-permuted: row r of the workgroup sits at tt*kRows + IO::drow(r), so
+    // that the rows one thread owns come in one or two vector reads a token ----
 #pragma unroll
     for (int q = 0; q < kDChunks; ++q) {
         const int i = t + q * kThreads;
-        if (i < n * kRow4) st4(d_l + 4 * i, rd[q]);
+        if (i < n * kRow4) {
+            const int tt = i / kRow4;
+            const int r = 4 * (i - tt * kRow4);
+            float* dp = d_l + tt * kRows;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[IO::drow(r + e)] = rd[q][e];
+        }
     }
 #pragma unroll
     for (int q = 0; q < kKChunks; ++q) {
@@ -390,61 +407,72 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
     }
     __syncthreads();
 
-    // ---- replay piece by piece, h = fma(delta_t[row], k_hat_t[col], h * g_t)
-    // for t < n: each piece waits only for its own load, so the replay of the
-    // first pieces overlaps the transfer of the later ones ----
+    // ---- replay, h = fma(delta_t[row], k_hat_t[col], h * g_t) for t < n,
+    // token by token over the thread's pieces ----
     f32x4 hb[ALIGN ? IO::kPer : 1];
-    if constexpr (sizeof(StateT) == 4) {
+    constexpr int kOwn = IO::kOwnRows;
+    static_assert(IO::kGroup * kOwn == kRows && kOwn % 2 == 0, "permuted correction rows");
+    const float* d_own = d_l + IO::drow(IO::local_row(t, 0));
+    for (int tt = 0; tt < n; ++tt) {
+        float d[kOwn];
+        if constexpr (kOwn % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < IO::kPer; ++i) {
-            const int row = IO::local_row(t, i);
-            for (int tt = 0; tt < n; ++tt) {
-                const f32x4 kh = ld4(k_l + tt * kDim + c0);
-                const float d = d_l[tt * kRows + row];
-                if constexpr (CH) {          // per-channel decay, column by column
-                    const f32x4 al = ld4(g_l + tt * kDim + c0);
+            for (int j = 0; j < kOwn; j += 4) {
+                const f32x4 x = ld4(d_own + tt * kRows + j);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * al[e]);
-                } else {
-                    const float g = g_l[tt];
+                for (int e = 0; e < 4; ++e) d[j + e] = x[e];
+            }
+        } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d, kh[e], h[i][e] * g);
-                }
-                if constexpr (ALIGN) {
-                    if (tt + 1 == bl) hb[i] = h[i];
-                }
+            for (int j = 0; j < kOwn; j += 2) {
+                const f32x2 x = *reinterpret_cast<const f32x2*>(d_own + tt * kRows + j);
+                d[j] = x.x;
+                d[j + 1] = x.y;
             }
         }
-    } else {
+        if constexpr (sizeof(StateT) == 4) {
+            const f32x4 kh = ld4(k_l + tt * kDim + c0);
+            if constexpr (CH) {          // per-channel decay, column by column
+                const f32x4 al = ld4(g_l + tt * kDim + c0);
 #pragma unroll
-        for (int i = 0; i < IO::kPer / 2; ++i) {
-            const int row = IO::local_row(t, i);
-            for (int tt = 0; tt < n; ++tt) {
-                const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
-                const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
-                const float d = d_l[tt * kRows + row];
-                if constexpr (CH) {
-                    const f32x4 al0 = ld4(g_l + tt * kDim + c0);
-                    const f32x4 al1 = ld4(g_l + tt * kDim + c0 + 4);
+                for (int i = 0; i < IO::kPer; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d[i], kh[e], h[i][e] * al[e]);
+            } else {
+                const float g = g_l[tt];
+#pragma unroll
+                for (int i = 0; i < IO::kPer; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[i][e] = __builtin_fmaf(d[i], kh[e], h[i][e] * g);
+            }
+        } else {
+            const f32x4 kh0 = ld4(k_l + tt * kDim + c0);
+            const f32x4 kh1 = ld4(k_l + tt * kDim + c0 + 4);
+            if constexpr (CH) {
+                const f32x4 al0 = ld4(g_l + tt * kDim + c0);
+                const f32x4 al1 = ld4(g_l + tt * kDim + c0 + 4);
+#pragma unroll
+                for (int i = 0; i < IO::kPer / 2; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * al0[e]);
-                        h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * al1[e]);
+                        h[2 * i][e] = __builtin_fmaf(d[i], kh0[e], h[2 * i][e] * al0[e]);
+                        h[2 * i + 1][e] = __builtin_fmaf(d[i], kh1[e], h[2 * i + 1][e] * al1[e]);
                     }
-                } else {
-                    const float g = g_l[tt];
+            } else {
+                const float g = g_l[tt];
+#pragma unroll
+                for (int i = 0; i < IO::kPer / 2; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        h[2 * i][e] = __builtin_fmaf(d, kh0[e], h[2 * i][e] * g);
-                        h[2 * i + 1][e] = __builtin_fmaf(d, kh1[e], h[2 * i + 1][e] * g);
+                        h[2 * i][e] = __builtin_fmaf(d[i], kh0[e], h[2 * i][e] * g);
+                        h[2 * i + 1][e] = __builtin_fmaf(d[i], kh1[e], h[2 * i + 1][e] * g);
                     }
-                }
-                if constexpr (ALIGN) {
-                    if (tt + 1 == bl) {
-                        hb[2 * i] = h[2 * i];
-                        hb[2 * i + 1] = h[2 * i + 1];
-                    }
-                }
+            }
+        }
+        if constexpr (ALIGN) {
+            if (tt + 1 == bl) {
+#pragma unroll
+                for (int i = 0; i < IO::kPer; ++i) hb[i] = h[i];
             }
         }
     }
@@ -508,9 +536,8 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
                            commit_lds_bytes(p.T, p.channel), s);
 }
 
-// Workgroups per head: the splits the launch chooses from (8 KiB per workgroup
-// for fp32 pools with up to 8 records and for bf16 pools, 32 KiB for fp32
-// pools with more records).
+// Workgroups per head: 8 KiB of state per workgroup, 8 per head for fp32 pools
+// and 4 for bf16 pools, whatever the record capacity.
 template <bool ALIGN>
 hipError_t launch_c_split(const CommitParams& p, bool bf16_state, hipStream_t s)
 {
@@ -518,9 +545,8 @@ hipError_t launch_c_split(const CommitParams& p, bool bf16_state, hipStream_t s)
         static_assert(kCommitSplitBf16 == 4, "bf16 split");
         return launch_c<uint16_t, ALIGN, kCommitSplitBf16>(p, s);
     }
-    static_assert(kCommitSplitF32 == 8 && kCommitSplitF32LongRecords == 2, "fp32 splits");
-    return p.T > 8 ? launch_c<float, ALIGN, kCommitSplitF32LongRecords>(p, s)
-                   : launch_c<float, ALIGN, kCommitSplitF32>(p, s);
+    static_assert(kCommitSplitF32 == 8, "fp32 split");
+    return launch_c<float, ALIGN, kCommitSplitF32>(p, s);
 }
 
 template <typename StateT>

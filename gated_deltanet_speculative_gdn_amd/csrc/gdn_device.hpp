@@ -26,6 +26,7 @@ constexpr int kRowSlot = 1, kRowWin = 2, kRowN = 4, kRowBnd = 8, kRowTable = 16,
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- bf16 ------------------------------------------------------------------

@@ -110,13 +110,12 @@ constexpr int kVerifyThreads = 256;
 // registers, which measured 2% faster (sweep of 0..34 KiB); bf16 pools run
 // best without a floor.
 constexpr int kVerifyLdsFloorF32 = 24 << 10;
-// Commit: workgroups per head for fp32 and bf16 pools (8 KiB per workgroup
-// streams best for fp32 at up to 8 records, 32 KiB at more; 8 KiB for bf16;
-// one workgroup per head measured slower for both); whether workgroup ids are
-// remapped XCD-contiguous. State loads and stores are always nontemporal
-// (cached streams measured slower).
+// Commit: workgroups per head for fp32 and bf16 pools (8 KiB of state per
+// workgroup streams best for both, at every record capacity, with the
+// token-by-token replay; one workgroup per head measured slower); whether
+// workgroup ids are remapped XCD-contiguous. State loads and stores are always
+// nontemporal (cached streams measured slower).
 constexpr int kCommitSplitF32 = 8;
-constexpr int kCommitSplitF32LongRecords = 2;   // fp32 pools with more than 8 records per row
 constexpr int kCommitSplitBf16 = 4;
 constexpr bool kCommitXcdRemap = true;
 
