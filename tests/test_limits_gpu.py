@@ -1,5 +1,6 @@
 """GPU parity at the interface's limits: the longest windows (T = 8 and 16
-records, every position in one window; fp32 and bf16 pools), a window placed
+records, every position in one window; fp32 and bf16 pools), record
+capacities 1, 3, 5 and 13 with align-mode boundaries, a window placed
 after pending records (record positions 5..15 verified after positions
 0..4), a commit over the most layers a pool set may hold (64), and key-head
 group sizes 1 to 12. Bars as in test_parity_gpu."""
@@ -29,6 +30,35 @@ def test_longest_windows(gdn, T, dtype):
     torch.cuda.synchronize()
     assert h.err_value() == 0
     check_layer(h, 0, np.arange(spec.rows), wl.n_accept, pre[0])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("T", [1, 3, 5, 13])
+def test_odd_record_capacities_with_boundaries(gdn, T, dtype):
+    """Record capacities off the 4/8/16 grid (the smaller members of each
+    compiled window capacity, so the commit's record staging meets partial
+    chunks), windows of T tokens, n from 1 to T (first row n = T, second
+    n = 1), and an align-mode boundary state after n - 1 tokens, written to a
+    spare slot, for every row with n >= 2."""
+    rows = 12
+    spec = W.shrink(W.SINGLE_LAYER, rows=rows, window=T, rec_tokens=T, n_lo=1, n_hi=T,
+                    num_slots=2 * rows)
+    wl = W.make_workload(spec, device="cuda", seed=120 + T, state_dtype=dtype)
+    n = wl.n_accept.copy()
+    n[0], n[1] = T, 1
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    torch.cuda.synchronize()
+    assert torch.equal(pool_bits(wl.state), pool_bits(pre))
+    bl = np.where(n >= 2, n - 1, 0).astype(np.int32)
+    spare = np.setdiff1d(np.arange(spec.num_slots), wl.state_slot)[:rows]
+    assert len(spare) == rows
+    bs = np.where(bl > 0, spare, -1).astype(np.int32)
+    h.commit(n=dev_i32(n), bnd_len=dev_i32(bl), bnd_slot=dev_i32(bs))
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    check_layer(h, 0, np.arange(rows), n, pre[0], bnd=(bl, bs))
 
 
 def test_window_after_pending_records(gdn):
