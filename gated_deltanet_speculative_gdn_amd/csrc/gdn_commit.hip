@@ -23,18 +23,20 @@
 // columns, so each token's key and decay are read from LDS once, and the
 // first token's pass waits for each piece's own load in turn, overlapping the
 // transfer of the later pieces. The final state is stored, then in align mode
-// the boundary state kept in a second register tile. State loads and stores are nontemporal (streamed past the caches:
-// nothing here is reused), and the workgroup ids are remapped so that each
-// XCD streams a contiguous range of heads. Because every thread reads all of
+// the boundary state kept in a second register tile. State loads and stores
+// are nontemporal (streamed past the caches: nothing here is reused), and the
+// workgroup ids are remapped so that each XCD streams a contiguous range of
+// heads. Because every thread reads all of
 // its source elements before its first store and writes only the elements it
 // read, a destination or boundary slot equal to the source slot is safe; the
 // pages' read-after-overwrite race between programs cannot occur.
 //
 // The same launch optionally carries the short conv's state compaction (extra
-// workgroups after the replay's) and serves two more record kinds: the payload
-// kind, whose replay recomputes each correction from the recorded key and
-// value, and the per-key-channel decay kind (a reading of Kimi-K3 KDA), whose
-// replay is h[v][k] = fma(delta[v], k_hat[k], h[v][k] * alpha[k]).
+// workgroups ahead of the replay's, so that their short copies overlap the
+// replay's ramp-up rather than its drain) and serves two more record kinds:
+// the payload kind, whose replay recomputes each correction from the recorded
+// key and value, and the per-key-channel decay kind (a reading of Kimi-K3
+// KDA), whose replay is h[v][k] = fma(delta[v], k_hat[k], h[v][k] * alpha[k]).
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
@@ -180,9 +182,13 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
 template <typename StateT, bool ALIGN, int SPLIT, bool CONV, bool PAY, bool CH>
 __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 {
+    // the conv compaction's workgroups come first, their count padded to a
+    // multiple of the XCD count so that the replay's ids below keep the
+    // hardware's round-robin XCD assignment
+    const int64_t conv_off = CONV ? (p.conv_wgs + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
     if constexpr (CONV) {
-        if ((int64_t)blockIdx.x >= p.ssm_wgs) {
-            conv_compact<ALIGN>(p, (int64_t)blockIdx.x - p.ssm_wgs);
+        if ((int64_t)blockIdx.x < conv_off) {
+            if ((int64_t)blockIdx.x < p.conv_wgs) conv_compact<ALIGN>(p, (int64_t)blockIdx.x);
             return;
         }
     }
@@ -196,7 +202,8 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                                       // per-channel records: [n][128] decays)
 
     // logical id: (layer, row, value head, part), XCD-contiguous
-    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(blockIdx.x, p.ssm_wgs) : blockIdx.x;
+    const int64_t wr = (int64_t)blockIdx.x - conv_off;
+    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(wr, p.ssm_wgs) : wr;
     const int part = (int)(wg % SPLIT);
     const int64_t head_id = wg / SPLIT;
     const int hv = (int)(head_id % p.hv);
@@ -523,7 +530,8 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
     CommitParams args = p;
     void* kargs[] = {&args};
     args.ssm_wgs = p.hv > 0 ? (int64_t)p.num_layers * p.num_rows * p.hv * SPLIT : 0;
-    const uint64_t grid = (uint64_t)(args.ssm_wgs + p.conv_wgs);
+    const int64_t conv_off = p.conv_wgs > 0 ? (p.conv_wgs + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
+    const uint64_t grid = (uint64_t)(args.ssm_wgs + conv_off);
     const bool conv = p.conv_wgs > 0;
     const void* fn =
         p.payload   ? (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, true, false>)

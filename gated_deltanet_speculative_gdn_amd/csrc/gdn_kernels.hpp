@@ -69,8 +69,9 @@ struct CommitParams {
     int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
     bool payload;             // payload records: the replay recomputes the corrections
     bool channel;             // per-channel decay records: alpha[T][K] in place of the gate
-    int64_t ssm_wgs;          // workgroups of the state replay (the first ones of the grid)
-    int64_t conv_wgs;         // workgroups of the conv compaction (after them; 0 = none)
+    int64_t ssm_wgs;          // workgroups of the state replay (after the conv's, below)
+    int64_t conv_wgs;         // workgroups of the conv compaction (0 = none); they come first
+                              // in the grid, their count padded to a multiple of the XCD count
     ConvParams conv;
 };
 
