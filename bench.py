@@ -10,8 +10,10 @@ the values.
 
 Prints one JSON line: state-updates/s (one update = one token applied to one
 128x128 head; verify counts every window token, commit every accepted token),
-per-kernel times from HIP events on the launch stream, the commit kernel's
-roofline against the 8 TB/s HBM peak, the native snapshot-every-token baseline
+per-kernel times from HIP events on the launch stream, the roofline of the
+step's dominant kernel (the one with the larger share of the step) against the
+8 TB/s HBM peak, with its rocprofv3 counter bytes when they were taken on this
+configuration and kernel source, the native snapshot-every-token baseline
 timed the same way, and the CPU oracle timed on the host's cores.
 """
 from __future__ import annotations
