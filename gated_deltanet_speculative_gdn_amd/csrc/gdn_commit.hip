@@ -129,9 +129,13 @@ __device__ int commit_row_error(const CommitParams& p, int b, int n, int src, in
 // Short-conv state compaction of one (layer, row, chunk of 256 16-byte column
 // pieces): row i of the final state is row n + i of [source rows 0..Ls-1,
 // inputs x_0..x_{n-1}], row i of the boundary state row bnd_len + i. Each
-// thread copies one column piece down the rows, final rows first, then the
-// boundary rows; it reads row n + i (or bnd_len + i > i) before it writes row
-// i, so a destination equal to the source is shifted in place correctly. No
+// thread copies one column piece down the rows, in ascending i; it reads row
+// n + i (or bnd_len + i > i) before it writes row i, so one state written over
+// its own source is shifted in place correctly. Both states must be formed
+// from unmodified source rows: when the final state goes into the source slot
+// (and the boundary, since it is written at all, into another slot), the
+// boundary rows are copied first; otherwise the final rows come first, and a
+// boundary written into the source slot then shifts it in place. No
 // arithmetic: the bytes are moved as they are.
 template <bool ALIGN>
 __device__ void conv_compact(const CommitParams& p, int64_t id)
@@ -170,13 +174,26 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
         return *reinterpret_cast<const u32x4*>(q);
     };
     char* dstp = pool + dst * slot_bytes;
-    for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(dstp + i * c.row_bytes) = row(n + i);
+    auto write_final = [&]() {
+        for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(dstp + i * c.row_bytes) = row(n + i);
+    };
     if constexpr (ALIGN) {
         if (bl > 0 && bs != dst) {
             char* bp = pool + bs * slot_bytes;
-            for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(bp + i * c.row_bytes) = row(bl + i);
+            auto write_bnd = [&]() {
+                for (int i = 0; i < Ls; ++i) *reinterpret_cast<u32x4*>(bp + i * c.row_bytes) = row(bl + i);
+            };
+            if (dst == src) {       // the final shift would overwrite rows the boundary reads
+                write_bnd();
+                write_final();
+            } else {
+                write_final();
+                write_bnd();
+            }
+            return;
         }
     }
+    write_final();
 }
 
 template <typename StateT, bool ALIGN, int SPLIT, bool CONV, bool PAY, bool CH>

@@ -201,19 +201,24 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
  * and write the state once, for every layer in one launch ([TS] Summary;
  * [vLLM] Purpose, Test Result).
  *
- * One 4-wave workgroup per (layer, row, value head). For row b (device int32
- * arrays [num_rows]):
+ * Launch shape: each (layer, row, value head) is split over several 4-wave
+ * workgroups, each owning a contiguous run of the head's rows (8 KiB of
+ * state: 8 workgroups of 16 rows for fp32 pools, 4 of 32 rows for bf16
+ * pools; [TS] uses one 4-warp block per head, the split streams faster on
+ * MI355X). For row b (device int32 arrays [num_rows]):
  *   n = n_accept[b]; if n == 0 or src_slot[b] < 0 nothing is read or written.
  *   h = state[l][src_slot[b]]; for t < n: h = fma(delta_t, k_hat_t^T, h * g_t)
  *   with the records of rec_slot[b] (per-channel decay records: h * alpha_t
- *   column by column; payload records: the correction recomputed first); the final h is written to dst_slot[b]
- *   (dst == src: in place). bf16 pools round once, to nearest even, here.
+ *   column by column; payload records: the correction recomputed first); the
+ *   final h is written to dst_slot[b] (dst == src: in place). bf16 pools
+ *   round once, to nearest even, here.
  *   Align mode (bnd_len and bnd_slot non-NULL): when 0 < bnd_len[b] < n the
  *   state after bnd_len[b] tokens is also written to bnd_slot[b], after the
  *   final state and from the same single read of the source, and not at all
- *   when bnd_slot[b] == dst_slot[b] ([vLLM] Commits item 6). Each workgroup
- *   reads its whole source head before its first store, so a boundary or
- *   final slot equal to the source slot is safe.
+ *   when bnd_slot[b] == dst_slot[b] ([vLLM] Commits item 6). Each thread
+ *   reads every source element it owns before its first store and writes only
+ *   those elements (a workgroup's rows are its own), so a boundary or final
+ *   slot equal to the source slot is safe.
  * Errors: GDN_ROW_SLOT, _N, _BND, _REC for bad device rows (row skipped).
  */
 int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
@@ -270,8 +275,13 @@ typedef struct gdn_conv_pools {
  *             [src rows 0..L_s-1, x[tok_start[b]] .. x[tok_start[b] + n - 1]]
  *   boundary: when 0 < bnd_len[b] < n and bnd_slot[b] != dst_slot[b], rows
  *             i of bnd_slot[b] = row bnd_len[b] + i of the same sequence,
- * final first, then boundary, each from values read before it is written over
- * (a final or boundary slot equal to the source slot is safe).
+ * both formed from the source rows as they were before the call. The final
+ * rows are written first, then the boundary rows, except when the final slot
+ * is the source slot: the boundary rows (then in another slot) go first, since
+ * the final shift overwrites source rows they are copied from. Either state
+ * written over its own source slot is shifted in place (row i is written only
+ * after row n + i, or bnd_len + i, has been read), so a final or boundary slot
+ * equal to the source slot is safe.
  * conv_tok_start: device int32 [num_rows], needed when conv is given.
  * Errors: as gdn_commit_all_layers; GDN_ROW_SLOT for conv slots outside
  * [0, conv->num_slots), GDN_ROW_WIN for a window outside x.

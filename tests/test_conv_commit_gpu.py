@@ -141,3 +141,65 @@ def test_fused_row_error_skips_both_parts(gdn):
     for b in (0, 1, 3):
         s = int(wl.state_slot[b])
         assert not torch.equal(pool_bits(cv.state[0, s]), pool_bits(pre_conv[0, s]))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_conv_slot_relations_from_caller(gdn, dtype):
+    """Slots chosen by the caller, not by the align plan: every relation the
+    ABI accepts between the source, final and boundary slots of a row, with
+    boundaries in (0, n). The case the plan never produces -- the final state
+    written in place (dst == src) with the boundary in another slot -- needs
+    the boundary rows copied before the in-place shift overwrites the source
+    rows they come from (vLLM RecoverSSM PR, Commits item 6: a fold reading a
+    source another fold has already overwritten)."""
+    rng = np.random.default_rng(73)
+    Ls, C, L = 5, 72, 2
+    # (n, bnd_len, relation) per row; slots are assigned below
+    rel = ["dst=src,bnd other", "bnd=src,dst other", "all distinct", "bnd=dst",
+           "dst=src,no bnd", "dst=src,bnd other"]
+    n = np.array([4, 3, 4, 2, 3, 2], np.int32)
+    bl = np.array([2, 1, 3, 1, 0, 1], np.int32)
+    rows = len(rel)
+    slots = 4 * rows
+    perm = rng.permutation(slots).astype(np.int32)
+    src = perm[:rows].copy()
+    dst = src.copy()
+    bs = np.full(rows, -1, np.int32)
+    spare = iter(perm[rows:])
+    for b, r in enumerate(rel):
+        if r.startswith("dst=src"):
+            dst[b] = src[b]
+            bs[b] = next(spare) if "bnd other" in r else -1
+        elif r == "bnd=src,dst other":
+            dst[b], bs[b] = next(spare), src[b]
+        elif r == "all distinct":
+            dst[b], bs[b] = next(spare), next(spare)
+        elif r == "bnd=dst":
+            dst[b] = next(spare)
+            bs[b] = dst[b]
+    assert (bl[bs < 0] == 0).all()
+    state = torch.randn((L, slots, Ls, C), device="cuda").to(dtype)
+    x = torch.randn((L, rows * 4, C), device="cuda").to(dtype)
+    ts = (np.arange(rows) * 4).astype(np.int32)
+    pre = raw(state)
+    xs = raw(x)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gdn_commit_all_layers_conv(None, G.ConvPools(state, x), dev_i32(src), dev_i32(dst), None,
+                                 dev_i32(n), dev_i32(bl), dev_i32(bs), dev_i32(ts),
+                                 err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = raw(state)
+    for layer in range(L):
+        for b in range(rows):
+            fin, bnd = oracle.conv_commit(pre[layer][src[b]], xs[layer][ts[b]: ts[b] + n[b]],
+                                          int(n[b]), int(bl[b]))
+            np.testing.assert_array_equal(got[layer][dst[b]], fin,
+                                          err_msg=f"layer {layer} row {b} ({rel[b]}) final")
+            if bnd is not None and bs[b] != dst[b]:
+                np.testing.assert_array_equal(got[layer][bs[b]], bnd,
+                                              err_msg=f"layer {layer} row {b} ({rel[b]}) boundary")
+        written = set(dst.tolist()) | set(bs[(bl > 0) & (bs != dst)].tolist())
+        for s in range(slots):
+            if s not in written:
+                np.testing.assert_array_equal(got[layer][s], pre[layer][s])
