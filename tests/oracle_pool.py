@@ -42,12 +42,26 @@ def gather(wl, layer, rows, T=None, state=None):
     beta ([R*HV] heads, row-major over (row, head)) and w."""
     s = wl.spec
     rows = np.asarray(rows)
-    R, HV, HK = len(rows), s.hv, s.hk
     tok = token_index(wl, rows, T)
-    T = tok.shape[1]
+    if s.ring_steps:
+        w = np.full(len(rows), tok.shape[1], np.int32)
+    else:
+        w = np.minimum(wl.win_len[rows], tok.shape[1]).astype(np.int32)
     pool = wl.state[layer] if state is None else state
     slots = torch.as_tensor(wl.state_slot[rows].astype(np.int64), device=pool.device)
-    S0 = to_f32(pool.index_select(0, slots)).reshape(R * HV, s.dv, s.dk)
+    S0 = to_f32(pool.index_select(0, slots)).reshape(len(rows) * s.hv, s.dv, s.dk)
+    return gather_tokens(wl, layer, tok, w, S0)
+
+
+def gather_tokens(wl, layer, tok, w, S0):
+    """Packed oracle inputs of rows whose tokens are ``tok`` [R][T] (token
+    indices into the workload's per-layer inputs), window lengths ``w`` [R] and
+    checkpoint heads ``S0`` [R*HV][V][K] (fp32)."""
+    s = wl.spec
+    tok = np.asarray(tok)
+    R, T = tok.shape
+    HV, HK = s.hv, s.hk
+    w = np.asarray(w, np.int32)
     tix = torch.as_tensor(tok.reshape(-1).astype(np.int64), device=wl.qkv.device)
     hk_of = np.arange(HV) // (HV // HK)
     q = to_f32(wl.q(layer).index_select(0, tix)).reshape(R, T, HK, s.dk)[:, :, hk_of]
@@ -55,10 +69,6 @@ def gather(wl, layer, rows, T=None, state=None):
     v = to_f32(wl.v(layer).index_select(0, tix)).reshape(R, T, HV, s.dv)
     a = to_f32(wl.a[layer].index_select(0, tix)).reshape(R, T, HV)
     beta = to_f32(wl.beta[layer].index_select(0, tix)).reshape(R, T, HV)
-    if s.ring_steps:
-        w = np.full(R, T, np.int32)
-    else:
-        w = np.minimum(wl.win_len[rows], T).astype(np.int32)
     return dict(
         S0=S0,
         q=np.ascontiguousarray(q.transpose(0, 2, 1, 3)).reshape(R * HV, T, s.dk),

@@ -19,7 +19,9 @@ import oracle_pool as OP
 import gated_deltanet_speculative_gdn_amd as G
 from gated_deltanet_speculative_gdn_amd import workloads as W
 from gpu_harness import Harness, dev_i32
-from test_parity_gpu import TOL, assert_bitwise, assert_close, check_bf16, pool_bits
+from test_parity_gpu import (TOL, assert_bitwise, assert_close, assert_close_blocks,
+                             assert_close_elementwise, assert_fp64_accuracy, check_bf16,
+                             pool_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,16 +51,20 @@ def check_channel_layer(h, a_ch, layer, rows, n, pre_state, *, T=None, bnd=None,
     if bnd is not None:
         keep.append(np.where(bnd[0] > 0, bnd[0], -1))
     g, res = OP.run_layer_ch(wl, a_ch, layer, rows, keep=np.stack(keep, 1), T=T, state=pre_state)
+    res64 = oracle.native_heads_ch(g["S0"], g["w"], g["q"], g["k"], g["v"], g["a"], g["beta"],
+                                   dtype=np.float64)
     Tw = g["q"].shape[1]
     valid = np.arange(Tw)[None, :] < g["w"][:, None]
-    o = h.outputs(layer, rows, T)
-    assert_close(np.where(valid[..., None], o, 0), np.where(valid[..., None], res.o, 0),
-                 f"layer {layer} outputs")
+    o = np.where(valid[..., None], h.outputs(layer, rows, T), 0)
+    assert_close(o, np.where(valid[..., None], res.o, 0), f"layer {layer} outputs")
+    assert_fp64_accuracy(o, res.o, res64.o, f"layer {layer} output vectors", mask=valid)
     d, kh, al = (x[:, :Tw] for x in channel_records(h, layer, rows))
     d, kh, al = (np.where(valid[..., None], x, 0).astype(np.float32) for x in (d, kh, al))
-    assert_close(d, res.rec_delta, f"layer {layer} corrections")
-    assert_close(kh, res.rec_khat, f"layer {layer} keys")
-    assert_close(al, res.rec_alpha, f"layer {layer} decays")
+    assert_close_blocks(d, res.rec_delta, 1, f"layer {layer} correction vectors")
+    assert_fp64_accuracy(d, res.rec_delta, res64.rec_delta, f"layer {layer} correction vectors",
+                         mask=valid)
+    assert_close_blocks(kh, res.rec_khat, 1, f"layer {layer} key vectors")
+    assert_close_elementwise(al, res.rec_alpha, f"layer {layer} decays")
     n = np.asarray(n)
     dst = wl.state_slot[rows] if dst is None else np.asarray(dst)
     live = n > 0
@@ -74,7 +80,7 @@ def check_channel_layer(h, a_ch, layer, rows, n, pre_state, *, T=None, bnd=None,
         rep = oracle.replay_heads_ch(g["S0"][sel], nn, d[sel], kh[sel], al[sel])
         if wl.state_dtype == torch.float32:
             got = h.heads(layer, slots)
-            assert_close(got, ref, f"layer {layer} {what} states")
+            assert_close_blocks(got, ref, 2, f"layer {layer} {what} state heads")
             assert_bitwise(got, rep, f"layer {layer} {what} vs replay of GPU records")
         else:
             check_bf16(h, layer, slots, rep, ref, what)
