@@ -14,7 +14,11 @@ per-kernel times from HIP events on the launch stream, the roofline of the
 step's dominant kernel (the one with the larger share of the step) against the
 8 TB/s HBM peak, with its rocprofv3 counter bytes when they were taken on this
 configuration and kernel source, the native snapshot-every-token baseline
-timed the same way, and the CPU oracle timed on the host's cores.
+timed the same way, the CPU oracle timed on the host's cores, and under
+"all_configs" the same step timing for every workload (fp32 state, and the
+batch-64 workload on a bf16 pool as well). Per-launch times are the means of
+the per-step HIP-event times (what rocprofv3's kernel averages match), with
+their medians beside them.
 """
 from __future__ import annotations
 
@@ -197,8 +201,10 @@ def accounting(wl, out_bytes=4, raw_gates=False, conv=None, rec_bytes=REC_TOKEN_
 
 
 def timed_loop(steps, graph_fn, eager_fn, graph_launches):
-    """Run `steps` steps of graph replay + one eager launch; return wall ms per
-    step and the mean per-launch event times of both parts."""
+    """Run `steps` steps of graph replay + one eager launch. Returns wall ms
+    per step (host clock over all steps, bracketed by synchronisation) and,
+    from HIP events on the launch stream, per-step arrays (ms) of the graph
+    part and of the eager launch."""
     sync = torch.cuda.synchronize
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -212,10 +218,14 @@ def timed_loop(steps, graph_fn, eager_fn, graph_launches):
         e2.record()
     sync()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    # per-launch times: averages over the timed steps
-    g_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    c_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
-    return wall, g_ms / graph_launches, c_ms, g_ms
+    g_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
+    c_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
+    return wall, g_ms, c_ms
+
+
+def summary_ms(x):
+    """Mean and median of per-step event times (ms)."""
+    return float(np.mean(x)), float(np.median(x))
 
 
 def capture(fn):
@@ -305,6 +315,115 @@ def counters_traffic(kernel, workload, launch_bytes, path=COUNTERS_FILE):
     return None
 
 
+def measure(spec, dtype, steps, warmup, gating="log", out_dtype="fp32", record="correction",
+            conv=False, accepted="uniform", eager=False):
+    """Build one workload on the device, warm up, capture the verify launches
+    of a step in a HIP graph and time `steps` steps (graph replay + the eager
+    all-layer commit). Returns the workload, its accounting, the Step and the
+    timings (means of the per-step event times, which rocprofv3's averages
+    match, and medians)."""
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
+    if accepted == "rates":
+        W.draw_acceptance_rate_counts(wl)
+    cv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if conv else None
+    payload = record == "payload"
+    channel = gating == "channel"
+    acc = accounting(wl, out_bytes=2 if out_dtype == "bf16" else 4, raw_gates=gating == "raw",
+                     conv=cv,
+                     rec_bytes=(PAYLOAD_TOKEN_BYTES if payload else
+                                CHANNEL_TOKEN_BYTES if channel else REC_TOKEN_BYTES),
+                     gate_bytes=CHANNEL_GATE_BYTES if channel else 8)
+    st = Step(wl, raw_gates=gating == "raw",
+              out_dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32, conv=cv,
+              record_kind=(G.RECORD_PAYLOAD if payload else
+                           G.RECORD_CHANNEL if channel else G.RECORD_CORRECTION))
+    launches = spec.layers * max(spec.ring_steps, 1)
+    # warm-up (also loads the code object before capture)
+    for _ in range(max(warmup, 1)):
+        st.verify_all()
+        st.commit()
+    torch.cuda.synchronize()
+    graph = capture(st.verify_all)
+    for _ in range(warmup):
+        graph.replay()
+        st.commit()
+    torch.cuda.synchronize()
+    wall, g_ms, c_ms = timed_loop(steps, graph.replay, st.commit, launches)
+    assert st.err.item() == 0, f"device row errors {st.err.item()}"
+    g_mean, g_med = summary_ms(g_ms)
+    c_mean, c_med = summary_ms(c_ms)
+    ver_ms, com_ms = g_mean / launches, c_mean
+    log(f"{spec.name} {'fp32' if dtype == torch.float32 else 'bf16'}: step {wall:.3f} ms: "
+        f"verify graph {g_mean:.3f} ms ({ver_ms * 1e3:.1f} us/layer), commit {com_ms * 1e3:.1f} us")
+    updates = acc["verify_updates"] + acc["commit_updates"]
+    com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
+    ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
+    kernels = {
+        "verify": {"us_per_launch": ver_ms * 1e3, "us_per_launch_median": g_med / launches * 1e3,
+                   "launches_per_step": launches,
+                   "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
+                   "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
+        "commit_all_layers": {"us_per_launch": com_ms * 1e3, "us_per_launch_median": c_med * 1e3,
+                              "launches_per_step": 1,
+                              "algorithmic_bytes_per_launch": acc["commit_bytes_per_launch"],
+                              "GB/s": com_gbs, "frac_of_peak": com_gbs / HBM_PEAK_GBS},
+    }
+    if eager:
+        # the same verify launches issued one by one, without the graph (outside
+        # the timed step): the host's launch cost per layer shows against the graph's
+        eager_steps = max(1, min(steps, 10))
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(eager_steps):
+            st.verify_all()
+        ev1.record()
+        torch.cuda.synchronize()
+        kernels["verify"]["eager_us_per_launch"] = ev0.elapsed_time(ev1) * 1e3 / (eager_steps * launches)
+        assert st.err.item() == 0, f"device row errors {st.err.item()}"
+    # the dominant kernel of the step: the one with the larger share of its time
+    if c_mean >= g_mean:
+        roofline = {"bound": "hbm", "kernel": "commit_all_layers", "achieved": com_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": com_gbs / HBM_PEAK_GBS}
+    else:
+        roofline = {"bound": "hbm", "kernel": "verify", "achieved": ver_gbs,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ver_gbs / HBM_PEAK_GBS}
+    step_bytes = launches * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]
+    del graph
+    return {"wl": wl, "acc": acc, "step": st, "launches": launches, "wall_ms": wall,
+            "step_ms_median": float(np.median(g_ms + c_ms)), "updates": updates,
+            "kernels": kernels, "roofline": roofline, "step_GB/s": step_bytes / (wall / 1e3) / 1e9}
+
+
+def all_configs(steps, warmup):
+    """Every workload (fp32 state, and the batch-64 workload on a bf16 pool too)
+    timed in this run the same way as the headline, without the native and CPU
+    legs: step time, per-launch verify and commit times (means and medians),
+    algorithmic GB/s and fraction of the HBM peak, the dominant kernel."""
+    out = {}
+    for spec in W.ORDERED:
+        for dtype in ((torch.float32, torch.bfloat16) if spec is W.MTP_B64 else (torch.float32,)):
+            name = spec.name + ("" if dtype == torch.float32 else "_bf16")
+            m = measure(spec, dtype, steps, warmup)
+            k = m["kernels"]
+            out[name] = {
+                "ms_per_step": m["wall_ms"], "ms_per_step_median": m["step_ms_median"],
+                "state_updates_per_s": m["updates"] / (m["wall_ms"] / 1e3),
+                "verify_us_per_launch": k["verify"]["us_per_launch"],
+                "verify_us_per_launch_median": k["verify"]["us_per_launch_median"],
+                "verify_launches_per_step": m["launches"],
+                "verify_GB/s": k["verify"]["GB/s"], "verify_frac": k["verify"]["frac_of_peak"],
+                "commit_us": k["commit_all_layers"]["us_per_launch"],
+                "commit_us_median": k["commit_all_layers"]["us_per_launch_median"],
+                "commit_GB/s": k["commit_all_layers"]["GB/s"],
+                "commit_frac": k["commit_all_layers"]["frac_of_peak"],
+                "dominant": m["roofline"]["kernel"], "dominant_frac": m["roofline"]["frac"],
+            }
+            del m
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +447,8 @@ def main():
                          "from per-position draft acceptance rates (.856/.694/.558 for the "
                          "three drafts of a 4-token window)")
     ap.add_argument("--no-native", action="store_true")
+    ap.add_argument("--no-all-configs", action="store_true",
+                    help="skip the per-configuration figures of every workload (profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="also time a plain device-to-device copy of this size: the measured "
@@ -353,68 +474,21 @@ def main():
     G.load_library()
     dtype = torch.float32 if args.state_dtype == "fp32" else torch.bfloat16
     log(f"workload {spec.name} ({spec.description}), state {args.state_dtype}")
-    wl = W.make_workload(spec, device="cuda", state_dtype=dtype)
-    if args.accepted == "rates":
-        W.draw_acceptance_rate_counts(wl)
-    conv = W.make_conv(wl, state_len=3, dtype=torch.bfloat16, device="cuda") if args.conv else None
     payload = args.record == "payload"
     channel = args.gating == "channel"
-    acc = accounting(wl, out_bytes=2 if args.out_dtype == "bf16" else 4,
-                     raw_gates=args.gating == "raw", conv=conv,
-                     rec_bytes=(PAYLOAD_TOKEN_BYTES if payload else
-                                CHANNEL_TOKEN_BYTES if channel else REC_TOKEN_BYTES),
-                     gate_bytes=CHANNEL_GATE_BYTES if channel else 8)
-    st = Step(wl, raw_gates=args.gating == "raw",
-              out_dtype=torch.bfloat16 if args.out_dtype == "bf16" else torch.float32, conv=conv,
-              record_kind=(G.RECORD_PAYLOAD if payload else
-                           G.RECORD_CHANNEL if channel else G.RECORD_CORRECTION))
-    L = spec.layers
-
-    # warm-up (also loads the code object before capture)
-    for _ in range(max(args.warmup, 1)):
-        st.verify_all()
-        st.commit()
-    torch.cuda.synchronize()
-    graph = capture(st.verify_all)
-    for _ in range(args.warmup):
-        graph.replay()
-        st.commit()
-    torch.cuda.synchronize()
-    launches = L * max(spec.ring_steps, 1)
-    wall, ver_ms, com_ms, graph_ms = timed_loop(args.steps, graph.replay, st.commit, launches)
-    assert st.err.item() == 0, f"device row errors {st.err.item()}"
-    log(f"step {wall:.3f} ms: verify graph {graph_ms:.3f} ms ({ver_ms * 1e3:.1f} us/layer), "
-        f"commit {com_ms * 1e3:.1f} us")
-
-    # the same verify launches issued one by one, without the graph (outside the
-    # timed step): the host's launch cost per layer shows against the graph's
-    eager_steps = max(1, min(args.steps, 10))
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(eager_steps):
-        st.verify_all()
-    ev1.record()
-    torch.cuda.synchronize()
-    ver_eager_us = ev0.elapsed_time(ev1) * 1e3 / (eager_steps * launches)
-    assert st.err.item() == 0, f"device row errors {st.err.item()}"
-
-    updates = acc["verify_updates"] + acc["commit_updates"]
+    m = measure(spec, dtype, args.steps, args.warmup, gating=args.gating,
+                out_dtype=args.out_dtype, record=args.record, conv=args.conv,
+                accepted=args.accepted, eager=True)
+    wl, acc, st, L, launches = m["wl"], m["acc"], m["step"], spec.layers, m["launches"]
+    wall, updates = m["wall_ms"], m["updates"]
     value = updates / (wall / 1e3)
-    com_gbs = acc["commit_bytes_per_launch"] / (com_ms / 1e3) / 1e9
-    ver_gbs = acc["verify_bytes_per_launch"] / (ver_ms / 1e3) / 1e9
-    step_gbs = (launches * acc["verify_bytes_per_launch"] + acc["commit_bytes_per_launch"]) / (wall / 1e3) / 1e9
     com_traffic = counters_traffic("commit_all_layers", spec.name, acc["commit_bytes_per_launch"])
     ver_traffic = counters_traffic("verify", spec.name, acc["verify_bytes_per_launch"])
-    # the dominant kernel of the step: the one with the larger share of its time
-    if com_ms >= graph_ms:
-        roofline = {"bound": "hbm", "kernel": "commit_all_layers", "achieved": com_gbs,
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": com_gbs / HBM_PEAK_GBS,
-                    "traffic": com_traffic}
-    else:
-        roofline = {"bound": "hbm", "kernel": "verify", "achieved": ver_gbs,
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ver_gbs / HBM_PEAK_GBS,
-                    "traffic": ver_traffic}
+    roofline = dict(m["roofline"])
+    roofline["traffic"] = com_traffic if roofline["kernel"] == "commit_all_layers" else ver_traffic
+    kern = m["kernels"]
+    kern["verify"]["counter_bytes_per_launch"] = ver_traffic
+    kern["commit_all_layers"]["counter_bytes_per_launch"] = com_traffic
 
     result = {
         "metric": "commit+verify state-updates/s and achieved HBM GB/s (% peak), B=64 D=4 48 layers",
@@ -438,21 +512,13 @@ def main():
                                 "rates " + "/".join(f"{r:g}" for r in
                                                     W.MTP_ACCEPTANCE_RATES[: spec.window - 1]))},
         "roofline": roofline,
-        "kernels": {
-            "verify": {"us_per_launch": ver_ms * 1e3, "launches_per_step": launches,
-                       "eager_us_per_launch": ver_eager_us,
-                       "algorithmic_bytes_per_launch": acc["verify_bytes_per_launch"],
-                       "counter_bytes_per_launch": ver_traffic,
-                       "GB/s": ver_gbs, "frac_of_peak": ver_gbs / HBM_PEAK_GBS},
-            "commit_all_layers": {"us_per_launch": com_ms * 1e3, "launches_per_step": 1,
-                                  "algorithmic_bytes_per_launch": acc["commit_bytes_per_launch"],
-                                  "counter_bytes_per_launch": com_traffic,
-                                  "GB/s": com_gbs, "frac_of_peak": com_gbs / HBM_PEAK_GBS},
-        },
-        "step_GB/s": step_gbs,
+        "kernels": kern,
+        "ms_per_step_median": m["step_ms_median"],
+        "step_GB/s": m["step_GB/s"],
         "updates_per_step": {"verify": acc["verify_updates"], "commit": acc["commit_updates"]},
         "kernel_source_hash": {k: source_hash(k) for k in KERNEL_SOURCES},
     }
+    del m
 
     if args.copy_probe_mib:
         nbytes = args.copy_probe_mib << 20
@@ -519,7 +585,8 @@ def main():
             native_graph.replay()
             st.native_accept()
         torch.cuda.synchronize()
-        nwall, nv_ms, na_ms, _ = timed_loop(args.steps, native_graph.replay, st.native_accept, L)
+        nwall, nv_arr, na_arr = timed_loop(args.steps, native_graph.replay, st.native_accept, L)
+        nv_ms, na_ms = float(np.mean(nv_arr)) / L, float(np.mean(na_arr))
         result["native_baseline"] = {
             "what": "same verify arithmetic writing the state after every draft token, "
                     "then one all-layer copy of the accepted state",
@@ -537,6 +604,12 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle on one full step ...")
         result["cpu_baseline"] = cpu_baseline(wl, acc, a_ch=st.a_ch)
+
+    if not args.no_all_configs:
+        del st, wl
+        torch.cuda.empty_cache()
+        log("every workload, the same step timing ...")
+        result["all_configs"] = all_configs(args.steps, args.warmup)
     print(json.dumps(result), flush=True)
 
 
