@@ -557,7 +557,9 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     }
     __syncthreads();
 
-    // ---- outputs and corrections of the owned rows, written out coalesced ----
+    // ---- outputs and corrections of the owned rows, written out coalesced and
+    // nontemporal (nothing in this launch reads them back; streaming them past
+    // the caches measured 1-2% faster) ----
     {
         constexpr int kRow4 = kRowsPerWg / 4;
         for (int i = tid; i < w * kRow4; i += NT) {
@@ -569,8 +571,8 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
                 *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + oo) =
                     u32x2{pack_bf16(ov.x, ov.y), pack_bf16(ov.z, ov.w)};
             else
-                st4(static_cast<float*>(p.out) + oo, ov);
-            if (!SNAP && !p.payload) st4(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kRowsPerWg + c));
+                st4_nt(static_cast<float*>(p.out) + oo, ov);
+            if (!SNAP && !p.payload) st4_nt(recb + (j0 + t) * kDim + row0 + c, ld4(L.dw + (j0 + t) * kRowsPerWg + c));
         }
     }
 

@@ -13,12 +13,14 @@ shared library and marshals numpy arrays:
 * :func:`replay_heads` -- replay of recorded tokens (the commit update).
 * :func:`native_heads_ch`, :func:`replay_heads_ch` -- the same with one decay
   per key channel (a reading of Kimi-K3 KDA, which the vLLM RecoverSSM PR's
-  Purpose names as a user of the same protocol without its arithmetic).
+  Purpose names as a user of the same protocol without its arithmetic; parity
+  unpinned against the pages).
 * :func:`align_plan` -- align-mode source / final / boundary slots, by walking
   token positions.
 * :func:`bf16_to_f32`, :func:`f32_to_bf16_rne` -- exact widening and
   round-to-nearest-even narrowing.
-* :func:`raw_gates` -- log-gate and write strength from raw gate inputs.
+* :func:`raw_gates` -- log-gate and write strength from raw gate inputs
+  (parity unpinned: the formula is a reading, the pages print none).
 * :func:`conv_decode`, :func:`conv_commit` -- the short-conv state, one token
   at a time (numpy; the state is a window of inputs, so this is data movement
   only).

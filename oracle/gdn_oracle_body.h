@@ -30,6 +30,17 @@
  * Every operation is one IEEE operation in REAL, rounded to nearest even; the
  * build turns floating-point contraction off, so only the fma written out is
  * fused. Sums run in ascending index order.
+ *
+ * PARITY UNPINNED against the pages (they print neither formula):
+ *   - raw_gate_: the decay and write strength formed from raw projections
+ *     (log-gate = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)) is the
+ *     parameterisation of [GDN]-style layers, a reading; its pieces are pinned
+ *     to closed forms and library identities, the choice of formula is not.
+ *   - native_head_ch_ / replay_head_ch_: one decay per key channel is this
+ *     build's reading of Kimi-K3 KDA, which [vLLM] Purpose names as a user of
+ *     the same protocol without giving its arithmetic; the rule is pinned to
+ *     its own fp64 transition-matrix form and to the scalar rule when every
+ *     channel decays alike, not to anything the pages print.
  */
 
 #define GLUE_(a, b) a##b
