@@ -16,7 +16,8 @@ step's dominant kernel (the one with the larger share of the step) against the
 configuration and kernel source, the native snapshot-every-token baseline
 timed the same way, the CPU oracle timed on the host's cores, and under
 "all_configs" the same step timing for every workload (fp32 state, and the
-batch-64 workload on a bf16 pool as well). Per-launch times are the means of
+batch-64 workload on a bf16 pool as well), each with the library's read probe
+timed over the bytes of one of its verify launches. Per-launch times are the means of
 the per-step HIP-event times (what rocprofv3's kernel averages match), with
 their medians beside them.
 """
@@ -395,6 +396,35 @@ def measure(spec, dtype, steps, warmup, gating="log", out_dtype="fp32", record="
             "kernels": kernels, "roofline": roofline, "step_GB/s": step_bytes / (wall / 1e3) / 1e9}
 
 
+_PROBE_BUF = {}
+
+
+def read_probe_at(nbytes, reps=10):
+    """Mean time of the library's read probe over `nbytes` (rounded down to the
+    probe's chunk), the reads rotating through a 1 GiB buffer so that no
+    repetition is served from the 256 MB cache: the read ceiling at the size of
+    one verify launch. Returns (bytes, us) or None."""
+    size = 1 << 30
+    vn = nbytes - nbytes % G.GDN_PROBE_CHUNK
+    if not 0 < vn <= size:
+        return None
+    if "a" not in _PROBE_BUF:
+        _PROBE_BUF["a"] = torch.zeros(size // 4, device="cuda")
+        _PROBE_BUF["sink"] = torch.empty(size // G.GDN_PROBE_CHUNK * 4, device="cuda")
+    a, sink = _PROBE_BUF["a"], _PROBE_BUF["sink"]
+    offs = [(i * vn) % (size - vn + 1) // 16 * 16 for i in range(reps)]
+    views = [a.view(torch.uint8)[o:o + vn] for o in offs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    G.gdn_bandwidth_probe(G.PROBE_READ, views[0], sink, vn)
+    torch.cuda.synchronize()
+    e0.record()
+    for v_ in views:
+        G.gdn_bandwidth_probe(G.PROBE_READ, v_, sink, vn)
+    e1.record()
+    torch.cuda.synchronize()
+    return vn, e0.elapsed_time(e1) * 1e3 / reps
+
+
 def all_configs(steps, warmup):
     """Every workload (fp32 state, and the batch-64 workload on a bf16 pool too)
     timed in this run the same way as the headline, without the native and CPU
@@ -419,6 +449,10 @@ def all_configs(steps, warmup):
                 "commit_frac": k["commit_all_layers"]["frac_of_peak"],
                 "dominant": m["roofline"]["kernel"], "dominant_frac": m["roofline"]["frac"],
             }
+            rp = read_probe_at(m["acc"]["verify_bytes_per_launch"])
+            if rp is not None:
+                out[name]["read_probe_at_verify_bytes_us"] = rp[1]
+                out[name]["verify_frac_of_read_probe"] = rp[1] / k["verify"]["us_per_launch"]
             del m
             torch.cuda.empty_cache()
     return out
@@ -610,6 +644,7 @@ def main():
         torch.cuda.empty_cache()
         log("every workload, the same step timing ...")
         result["all_configs"] = all_configs(args.steps, args.warmup)
+        _PROBE_BUF.clear()
     print(json.dumps(result), flush=True)
 
 
