@@ -187,7 +187,6 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     v.num_slots = pools->num_state_slots;
     v.num_rec_slots = pools->num_rec_slots;
     v.T = pools->rec_tokens;
-    v.lds_floor = (pools->state_dtype == GDN_STATE_F32 && v.T <= 4) ? kVerifyLdsFloorF32 : 0;
     return launched(launch_verify(v, pools->state_dtype == GDN_STATE_BF16, (hipStream_t)stream));
 }
 

@@ -36,7 +36,6 @@ struct VerifyParams {
     bool payload;             // payload records (k, v, gate, beta) instead of corrections
     bool channel;             // one decay per key channel: a_log is [tokens][HV][K] with
     int64_t a_ts;             //   token stride a_ts; records hold alpha[T][K] for the gate
-    int32_t lds_floor;        // launch: at least this much dynamic LDS (bytes; 0 = the default)
 };
 
 // Short-conv state compaction, run by extra workgroups of the commit launch:
@@ -101,16 +100,14 @@ struct PlanParams {
 constexpr int kMaxRecTokens = GDN_MAX_REC_TOKENS;
 
 // Verify launch shape: rows of a head each thread holds and threads per
-// workgroup; a workgroup covers threads/8 * R rows (here 64: two workgroups
-// per head). One and four rows per thread and 512-thread workgroups measured
-// no faster.
+// workgroup; a workgroup covers threads/8 * R rows. Windows of up to 4
+// positions (the MTP shape) run 512-thread workgroups, one per head (bf16
+// pools 3.4% and fp32 pools 0.6% faster than two 256-thread workgroups per
+// head); longer windows, whose LDS staging is larger, run two 256-thread
+// workgroups per head. One and four rows per thread measured no faster.
 constexpr int kVerifyRowsPerThread = 2;
-constexpr int kVerifyThreads = 256;
-// Verify on fp32 pools with short windows (T <= 4) asks for at least this much
-// dynamic LDS: it then runs six workgroups per CU, set by LDS rather than by
-// registers, which measured 2% faster (sweep of 0..34 KiB); bf16 pools run
-// best without a floor.
-constexpr int kVerifyLdsFloorF32 = 24 << 10;
+constexpr int kVerifyThreadsShort = 512;   // windows of up to 4 positions
+constexpr int kVerifyThreads = 256;        // longer windows
 // Commit: workgroups per head for fp32 and bf16 pools (8 KiB of state per
 // workgroup streams best for both, at every record capacity, with the
 // token-by-token replay; one workgroup per head measured slower); whether

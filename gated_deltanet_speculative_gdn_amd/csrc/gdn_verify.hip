@@ -29,7 +29,9 @@
 // vector fmas it saves. So the contraction stays on the vector ALU, fused with
 // the recurrence in registers.
 //
-// One workgroup of four wave64s per (row, value head, chunk of 32*R head rows);
+// One workgroup per (row, value head, chunk of NT/8*R head rows): eight wave64s
+// covering the whole head for windows of up to 4 positions, four wave64s per
+// half head for longer ones;
 // workgroup ids are remapped so that each XCD streams a contiguous stretch of
 // the pool. Thread t holds head rows row0 + R*(t/8) + r and columns
 // 4*(t%8) + 32*c + e (c, e = 0..3): each 16-byte load of eight neighbouring
@@ -616,8 +618,7 @@ hipError_t launch_tt(const VerifyParams& p, hipStream_t s)
     void* kargs[] = {&args};
     const unsigned chunks = kDim / (NT / 8 * R);
     const unsigned grid = (unsigned)(p.num_rows * p.hv) * chunks;
-    const size_t need = sizeof(float) * Lds<TT, NT / 8 * R, CH, SNAP>::kFloats;
-    const size_t lds = need > (size_t)p.lds_floor ? need : (size_t)p.lds_floor;
+    const size_t lds = sizeof(float) * Lds<TT, NT / 8 * R, CH, SNAP>::kFloats;
     return hipLaunchKernel(reinterpret_cast<const void*>(&verify_kernel<StateT, SNAP, R, NT, TT, CH>),
                            dim3(grid), dim3(NT), kargs, lds, s);
 }
@@ -627,7 +628,7 @@ template <typename StateT, bool SNAP, bool CH>
 hipError_t launch_ch(const VerifyParams& p, hipStream_t s)
 {
     constexpr int R = kVerifyRowsPerThread, NT = kVerifyThreads;
-    if (p.T <= 4) return launch_tt<StateT, SNAP, R, NT, 4, CH>(p, s);
+    if (p.T <= 4) return launch_tt<StateT, SNAP, R, kVerifyThreadsShort, 4, CH>(p, s);
     if (p.T <= 8) return launch_tt<StateT, SNAP, R, NT, 8, CH>(p, s);
     return launch_tt<StateT, SNAP, R, NT, kMaxRecTokens, CH>(p, s);
 }

@@ -116,3 +116,27 @@ def test_key_head_groups(gdn, hv, hk):
     torch.cuda.synchronize()
     assert h.err_value() == 0
     check_layer(h, 0, np.arange(spec.rows), wl.n_accept, pre[0])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_grids_not_a_multiple_of_the_xcd_count(gdn, dtype):
+    """Launches whose workgroup count is not a multiple of the 8 XCDs, so the
+    XCD-contiguous id remap leaves a tail of ids mapped to themselves: 3 layers
+    x 5 rows x 3 value heads gives verify grids of 30 (tail 6) and, on bf16
+    pools (4 workgroups per head), a commit grid of 180 (tail 4). Every layer
+    against the oracle, every slot outside the write set unchanged."""
+    spec = W.shrink(W.ALL_LAYER, layers=3, rows=5, hv=3, hk=3, num_slots=16)
+    wl = W.make_workload(spec, device="cuda", state_dtype=dtype, seed=131)
+    h = Harness(wl)
+    pre = wl.state.clone()
+    h.verify_all()
+    h.commit()
+    torch.cuda.synchronize()
+    assert h.err_value() == 0
+    for layer in range(spec.layers):
+        check_layer(h, layer, np.arange(spec.rows), wl.n_accept, pre[layer])
+    live = {int(s) for s, n in zip(wl.state_slot, wl.n_accept) if n > 0}
+    for layer in range(spec.layers):
+        for s in range(spec.num_slots):
+            if s not in live:
+                assert torch.equal(pool_bits(wl.state[layer, s]), pool_bits(pre[layer, s])), (layer, s)
