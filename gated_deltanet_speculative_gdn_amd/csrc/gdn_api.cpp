@@ -156,7 +156,8 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     int32_t st = check_pools(pools);
     if (st) return st;
     if (layer < 0 || layer >= pools->num_layers || num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads * 4 > INT32_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)num_rows * pools->num_v_heads * kVerifyItemsPerHead > (int64_t)0xFFFFFFFFu)
+        return GDN_ERR_SHAPE;
     if ((st = check_layer_ptrs(pools, layer, true))) return st;
     if ((st = check_io(io))) return st;
     if (!state_slot || !rec_slot || !tok_start || !win_len) return GDN_ERR_NULL;
@@ -198,7 +199,8 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
     int32_t st = check_pools(pools);
     if (st) return st;
     if (layer < 0 || layer >= pools->num_layers || num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads * 4 > INT32_MAX) return GDN_ERR_SHAPE;
+    if ((int64_t)num_rows * pools->num_v_heads * kVerifyItemsPerHead > (int64_t)0xFFFFFFFFu)
+        return GDN_ERR_SHAPE;
     if ((st = check_layer_ptrs(pools, layer, false))) return st;
     if ((st = check_io(io))) return st;
     if (!state_slot || !tok_start || !win_len || !snap) return GDN_ERR_NULL;
@@ -249,15 +251,17 @@ int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools*
     }
     if (num_rows < 0) return GDN_ERR_SHAPE;
     const int32_t layers = pools ? pools->num_layers : conv->num_layers;
-    int64_t wgs = 0;
-    if (pools) wgs += (int64_t)num_rows * pools->num_v_heads * layers * 8;
+    // one layer's workgroups must fit in one launch (the launcher splits the
+    // layers over several launches when all of them do not)
+    int64_t layer_wgs = 0;
+    if (pools) layer_wgs += (int64_t)num_rows * pools->num_v_heads * kCommitSplitF32;
     int64_t conv_per_row = 0;
     if (conv) {
         const int64_t pieces = conv_row_bytes(conv) / 16;
         conv_per_row = (pieces + kConvPiecesPerWg - 1) / kConvPiecesPerWg;
-        wgs += (int64_t)num_rows * layers * conv_per_row;
+        layer_wgs += (int64_t)num_rows * conv_per_row;
     }
-    if (wgs > INT32_MAX) return GDN_ERR_SHAPE;
+    if (layer_wgs > kMaxLaunchWgs - 8) return GDN_ERR_SHAPE;
     if (!src_slot || !dst_slot || !n_accept) return GDN_ERR_NULL;
     if ((bnd_len == nullptr) != (bnd_slot == nullptr)) return GDN_ERR_NULL;
     if (num_rows == 0) return GDN_OK;
@@ -324,7 +328,7 @@ int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers, int3
     int32_t st = check_pools(pools);
     if (st) return st;
     if (num_rows < 0) return GDN_ERR_SHAPE;
-    if ((int64_t)num_rows * pools->num_v_heads * pools->num_layers > INT32_MAX)
+    if ((int64_t)num_rows * pools->num_v_heads * pools->num_layers > kMaxLaunchWgs)
         return GDN_ERR_SHAPE;
     if (!snap_layers || !dst_slot || !n_accept) return GDN_ERR_NULL;
     for (int32_t l = 0; l < pools->num_layers; ++l) {

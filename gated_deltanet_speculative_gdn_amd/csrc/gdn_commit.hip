@@ -544,11 +544,7 @@ __global__ void __launch_bounds__(kThreads) accept_kernel(AcceptParams p)
 template <typename StateT, bool ALIGN, int SPLIT>
 hipError_t launch_c(const CommitParams& p, hipStream_t s)
 {
-    CommitParams args = p;
-    void* kargs[] = {&args};
-    args.ssm_wgs = p.hv > 0 ? (int64_t)p.num_layers * p.num_rows * p.hv * SPLIT : 0;
-    const int64_t conv_off = p.conv_wgs > 0 ? (p.conv_wgs + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
-    const uint64_t grid = (uint64_t)(args.ssm_wgs + conv_off);
+    static_assert(kThreads == kCommitThreads, "launch limit counted for 256-thread workgroups");
     const bool conv = p.conv_wgs > 0;
     const void* fn =
         p.payload   ? (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, true, false>)
@@ -557,8 +553,33 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
                             : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false, true>))
                     : (conv ? reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, true, false, false>)
                             : reinterpret_cast<const void*>(&commit_kernel<StateT, ALIGN, SPLIT, false, false, false>));
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs,
-                           commit_lds_bytes(p.T, p.channel), s);
+    // workgroups of one layer: the state replay's and the conv compaction's
+    const int64_t ssm_layer = p.hv > 0 ? (int64_t)p.num_rows * p.hv * SPLIT : 0;
+    const int64_t conv_layer = conv ? (int64_t)p.num_rows * p.conv.wgs_per_row : 0;
+    // layers per launch: all of them unless the grid would pass the
+    // dispatch limit (the host entry point has checked that one layer fits)
+    const int64_t per = (kMaxLaunchWgs - kNumXcd) / (ssm_layer + conv_layer);
+    const int step = per >= p.num_layers ? p.num_layers : (int)per;
+    for (int l0 = 0; l0 < p.num_layers; l0 += step) {
+        CommitParams args = p;
+        const int nl = p.num_layers - l0 < step ? p.num_layers - l0 : step;
+        for (int l = 0; l < nl; ++l) {
+            args.state[l] = p.state[l0 + l];
+            args.rec[l] = p.rec[l0 + l];
+            args.conv.state[l] = p.conv.state[l0 + l];
+            args.conv.x[l] = p.conv.x[l0 + l];
+        }
+        args.num_layers = nl;
+        args.ssm_wgs = ssm_layer * nl;
+        args.conv_wgs = conv_layer * nl;
+        const int64_t conv_off = conv ? (args.conv_wgs + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
+        const uint64_t grid = (uint64_t)(args.ssm_wgs + conv_off);
+        void* kargs[] = {&args};
+        const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs,
+                                             commit_lds_bytes(p.T, p.channel), s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Workgroups per head: 8 KiB of state per workgroup, 8 per head for fp32 pools

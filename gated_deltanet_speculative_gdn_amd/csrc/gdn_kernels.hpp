@@ -116,6 +116,16 @@ constexpr int kVerifyThreads = 256;        // longer windows
 constexpr int kCommitSplitF32 = 8;
 constexpr int kCommitSplitBf16 = 4;
 constexpr bool kCommitXcdRemap = true;
+// The dispatch packet counts a launch's work-items (workgroups x threads) in 32
+// bits, so one launch of 256-thread workgroups holds at most this many. The
+// all-layer commit issues consecutive launches over runs of whole layers when
+// its grid would exceed it (fp32 pools: beyond 2^21 (layer, row, head) triples,
+// 137 GB of source state); one layer must fit in one launch.
+constexpr int64_t kCommitThreads = 256;
+constexpr int64_t kMaxLaunchWgs = (int64_t)0xFFFFFFFFu / kCommitThreads;
+// Verify: a layer's launch is rows x value heads x 512 work-items (one 512-thread
+// workgroup or two 256-thread ones per head).
+constexpr int64_t kVerifyItemsPerHead = 512;
 
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_verify(const VerifyParams& p, bool bf16_state, hipStream_t s);

@@ -187,8 +187,10 @@ typedef struct gdn_verify_io {
  *   writes o_t into io->out and the record (delta, k_hat, gate; or with the
  *   payload record kind k, v, gate, beta) at position rec_base + t. The
  *   state pool is never written.
- * Errors: GDN_ERR_* as in the conventions; device rows with a bad slot,
- * window or record slot are skipped with GDN_ROW_SLOT / _WIN / _REC.
+ * Errors: GDN_ERR_* as in the conventions (GDN_ERR_SHAPE also when
+ * num_rows * HV * 512 exceeds 2^32 - 1, the work-items one launch may hold);
+ * device rows with a bad slot, window or record slot are skipped with
+ * GDN_ROW_SLOT / _WIN / _REC.
  */
 int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
                    const int32_t* state_slot, const int32_t* rec_slot,
@@ -219,6 +221,12 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
  *   reads every source element it owns before its first store and writes only
  *   those elements (a workgroup's rows are its own), so a boundary or final
  *   slot equal to the source slot is safe.
+ * Launches: one, unless the grid would exceed the 2^32 - 1 work-items one
+ *   launch may hold (fp32 pools: more than 2^21 (layer, row, value head)
+ *   triples); then consecutive launches on `stream`, each over a run of whole
+ *   layers (a launch that fails returns GDN_ERR_LAUNCH after the earlier
+ *   ones have been issued). One layer's workgroups (num_rows * HV * 8, plus
+ *   the conv compaction's) must fit in one launch, else GDN_ERR_SHAPE.
  * Errors: GDN_ROW_SLOT, _N, _BND, _REC for bad device rows (row skipped).
  */
 int32_t gdn_commit_all_layers(const gdn_pools* pools, int32_t num_rows,
@@ -353,7 +361,8 @@ int32_t gdn_check_slots(int32_t num_rows, const int32_t* src_slot, const int32_t
  * snap: device, [num_rows][HV][T][V][K] in the pool's state dtype (T =
  *   pools->rec_tokens); snap[b][h][t] = state after token t of row b, rounded
  *   to bf16 for bf16 pools. 16-byte aligned. No record is written.
- * Rows: as gdn_verify without record slot and ring base.
+ * Rows: as gdn_verify without record slot and ring base (and its limit on
+ * num_rows * HV).
  */
 int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_rows,
                           const int32_t* state_slot, const int32_t* tok_start,
@@ -364,7 +373,8 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
  * gdn_native_accept -- the baseline's state copy: for every layer, row b
  * with n = n_accept[b] >= 1 copies snap_layers[l][b][h][n-1] into
  * state[l][dst_slot[b]][h]. snap_layers: host array of num_layers device
- * pointers laid out as in gdn_native_window.
+ * pointers laid out as in gdn_native_window. One 256-thread workgroup per
+ * (layer, row, head): GDN_ERR_SHAPE when there are more than (2^32 - 1) / 256.
  */
 int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers,
                           int32_t num_rows, const int32_t* dst_slot,

@@ -210,6 +210,27 @@ def test_commit_rejects_malformed(lib):
     assert commit(lib, p) == E_SHAPE
 
 
+def test_launch_size_limits(lib):
+    """A launch counts its work-items in 32 bits. Verify (and the native
+    window) run 512 work-items per (row, value head): 2^32 / 512 = 8,388,608
+    pairs is one too many. The commit splits its layers over several launches,
+    but one layer (8 workgroups of 256 per head, plus 8 of padding) must fit:
+    2,097,151 pairs is the most. The native accept copy is one workgroup per
+    (layer, row, head). Rejected calls launch nothing (the pointers are fake)."""
+    p = good_pools()
+    p.num_v_heads, p.num_k_heads = 64, 64
+    io = good_io()
+    rows = 8_388_608 // 64
+    assert verify(lib, p, io, rows=rows) == E_SHAPE
+    assert lib.gdn_native_window(C.byref(p), 0, rows, ROWS, ROWS, ROWS, C.byref(io),
+                                 C.c_void_p(0xA0000), None, None) == E_SHAPE
+    rows = 2_097_152 // 64
+    assert commit(lib, p, rows=rows) == E_SHAPE
+    snaps = (C.c_void_p * 2)(0xB0000, 0xC0000)
+    rows = 16_777_216 // (64 * 2)                      # two layers
+    assert lib.gdn_native_accept(C.byref(p), snaps, rows, ROWS, ROWS, None, None) == E_SHAPE
+
+
 def test_align_plan_rejects_malformed(lib):
     def plan(rows=4, stride=8, cols=8, block=64, max_n=16, table=ROWS):
         return lib.gdn_align_plan(rows, ROWS, ROWS, table, stride, cols, block, max_n,

@@ -2,16 +2,19 @@
 records, every position in one window; fp32 and bf16 pools), record
 capacities 1, 3, 5 and 13 with align-mode boundaries, a window placed
 after pending records (record positions 5..15 verified after positions
-0..4), a commit over the most layers a pool set may hold (64), and key-head
-group sizes 1 to 12. Bars as in test_parity_gpu."""
+0..4), a commit over the most layers a pool set may hold (64), key-head
+group sizes 1 to 12, grids that are not a multiple of the XCD count, and a
+commit too large for one launch. Bars as in test_parity_gpu."""
 import numpy as np
 import pytest
 import torch
 
 import gated_deltanet_speculative_gdn_amd as G
+import oracle
 from gated_deltanet_speculative_gdn_amd import workloads as W
 from gpu_harness import Harness, dev_i32
-from test_parity_gpu import check_layer, pool_bits
+from oracle_pool import to_f32
+from test_parity_gpu import assert_bitwise, check_layer, pool_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +143,67 @@ def test_grids_not_a_multiple_of_the_xcd_count(gdn, dtype):
         for s in range(spec.num_slots):
             if s not in live:
                 assert torch.equal(pool_bits(wl.state[layer, s]), pool_bits(pre[layer, s])), (layer, s)
+
+
+@pytest.mark.parametrize("dtype,rows", [(torch.float32, 21846), (torch.bfloat16, 43691)],
+                         ids=["fp32", "bf16"])
+def test_commit_beyond_one_launch(gdn, dtype, rows):
+    """An all-layer commit whose grid passes the 2^32 - 1 work-items one launch
+    may hold: 3 layers x rows x 32 value heads is 16,777,728 workgroups on fp32
+    pools (8 per head) and 16,777,344 on bf16 pools (4 per head), so the
+    library issues two launches, layers 0-1 and layer 2. Five live rows per
+    layer, at the start, the middle and the end (the last is the grid's last
+    workgroup), in place and into other slots; every other row n = 0. The
+    records are seeded directly (corrections, unit keys, decays in (0.2, 1)):
+    every committed head equals the oracle's replay of them bit for bit (bf16
+    pools: its RNE), and every other slot is unchanged."""
+    L, HV, HK, T = 3, 32, 16, 4
+    live = np.array([0, 1, rows // 2, rows - 2, rows - 1])
+    nl = len(live)
+    num_slots = 2 * nl
+    print(f"commit over {L * rows * HV} heads, {dtype}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(140)
+    state = (torch.randn((L, num_slots, HV, 128, 128), generator=gen, device="cuda")
+             * 0.05).to(dtype)
+    d = torch.randn((L, nl, HV, T, 128), generator=gen, device="cuda") * 0.1
+    k = torch.nn.functional.normalize(
+        torch.randn((L, nl, HV, T, 128), generator=gen, device="cuda"), dim=-1)
+    g = torch.rand((L, nl, HV, T), generator=gen, device="cuda") * 0.8 + 0.2
+    rec = G.Pools.alloc_records(L, nl, HV, T)
+    rec[..., : T * 128] = d.reshape(L, nl, HV, T * 128)
+    rec[..., T * 128: 2 * T * 128] = k.reshape(L, nl, HV, T * 128)
+    rec[..., 2 * T * 128: 2 * T * 128 + T] = g
+    pools = G.Pools(state, rec, HK, T)
+    src = np.full(rows, -1, np.int32)
+    dst = np.full(rows, -1, np.int32)
+    rs = np.zeros(rows, np.int32)
+    n = np.zeros(rows, np.int32)
+    src[live] = np.arange(nl)
+    dst[live] = [0, nl + 1, 2, nl + 3, nl + 4]          # in place and moved
+    rs[live] = np.arange(nl)
+    n[live] = [4, 1, 3, 2, 4]
+    pre = state.clone()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gdn_commit_all_layers(pools, dev_i32(src), dev_i32(dst), dev_i32(rs), dev_i32(n),
+                            err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    written = set(int(x) for x in dst[live])
+    for layer in range(L):
+        for i, b in enumerate(live):
+            S0 = to_f32(pre[layer, src[b]]).reshape(HV, 128, 128)
+            rep = oracle.replay_heads(S0, np.full(HV, n[b], np.int32),
+                                      d[layer, i].cpu().numpy(), k[layer, i].cpu().numpy(),
+                                      g[layer, i].cpu().numpy())
+            got = state[layer, dst[b]]
+            if dtype == torch.float32:
+                assert_bitwise(got.cpu().numpy().reshape(HV, 128, 128), rep,
+                               f"layer {layer} row {b}")
+            else:
+                bits_ = got.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                assert_bitwise(bits_.reshape(HV, 128, 128), oracle.f32_to_bf16_rne(rep),
+                               f"layer {layer} row {b}")
+        keep = [s for s in range(num_slots) if s not in written]
+        idx = torch.as_tensor(keep, device="cuda")
+        assert torch.equal(pool_bits(state[layer].index_select(0, idx)),
+                           pool_bits(pre[layer].index_select(0, idx))), f"layer {layer}"
