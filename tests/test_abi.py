@@ -215,7 +215,7 @@ def test_launch_size_limits(lib):
     window) run 512 work-items per (row, value head): 2^32 / 512 = 8,388,608
     pairs is one too many. The commit splits its layers over several launches,
     but one layer (8 workgroups of 256 per head, plus 8 of padding) must fit:
-    2,097,151 pairs is the most. The native accept copy is one workgroup per
+    2,097,150 pairs is the most. The native accept copy is one workgroup per
     (layer, row, head). Rejected calls launch nothing (the pointers are fake)."""
     p = good_pools()
     p.num_v_heads, p.num_k_heads = 64, 64
