@@ -64,7 +64,21 @@
 namespace gdn {
 namespace {
 
-// ---- register tile of R rows: h[r][c] = row row0 + R*grp + r, columns 4*lane8 + 32*c .. +3
+// ---- register tile of R rows: h[r][c] = row row0 + R*grp + r, the four
+// columns tcol<StateT>(lane8, c) .. +3. Each load instruction of an 8-lane
+// group reads 128 contiguous bytes of a row: fp32 pools 16 bytes a lane, chunk
+// c at column 32c + 4 lane8; bf16 pools 16 bytes (eight values) a lane, chunk
+// pair (2m, 2m+1) at column 64m + 8 lane8. (Eight-byte bf16 pieces in the fp32
+// column order read 64-byte segments and made the bf16 verify about 5%
+// slower.) The lanes' partial sums therefore cover other columns on bf16
+// pools than on fp32 pools: the two paths agree to rounding, not bit for bit.
+template <typename StateT> __device__ __forceinline__ int tcol(int lane8, int c);
+template <> __device__ __forceinline__ int tcol<float>(int lane8, int c) { return 4 * lane8 + 32 * c; }
+template <> __device__ __forceinline__ int tcol<uint16_t>(int lane8, int c)
+{
+    return 8 * lane8 + 64 * (c >> 1) + 4 * (c & 1);
+}
+
 template <typename StateT, int R> struct TileIO;
 
 template <int R> struct TileIO<float, R> {
@@ -73,28 +87,29 @@ template <int R> struct TileIO<float, R> {
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                h[r][c] = ld4_nt(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c);
+                h[r][c] = ld4_nt(head + (row0 + R * grp + r) * kDim + tcol<float>(lane8, c));
     }
     __device__ static void store(float* head, int row0, int grp, int lane8, const f32x4 (&h)[R][4]) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                st4_nt(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c, h[r][c]);
+                st4_nt(head + (row0 + R * grp + r) * kDim + tcol<float>(lane8, c), h[r][c]);
     }
 };
 
-// bf16 pool: the same element ownership, 8-byte pieces (four bf16 values).
+// bf16 pool: one 16-byte piece (eight values) per chunk pair, widened exactly.
 template <int R> struct TileIO<uint16_t, R> {
     __device__ static void load(const uint16_t* head, int row0, int grp, int lane8,
                                 f32x4 (&h)[R][4]) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-                    head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c));
-                h[r][c] = f32x4{bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
+            for (int m = 0; m < 2; ++m) {
+                const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                    head + (row0 + R * grp + r) * kDim + tcol<uint16_t>(lane8, 2 * m)));
+                h[r][2 * m] = f32x4{bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y)};
+                h[r][2 * m + 1] = f32x4{bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
             }
     }
     __device__ static void store(uint16_t* head, int row0, int grp, int lane8,
@@ -102,11 +117,13 @@ template <int R> struct TileIO<uint16_t, R> {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const f32x4 v = h[r][c];
+            for (int m = 0; m < 2; ++m) {
+                const f32x4 v = h[r][2 * m], u = h[r][2 * m + 1];
                 __builtin_nontemporal_store(
-                    u32x2{pack_bf16(v.x, v.y), pack_bf16(v.z, v.w)},
-                    reinterpret_cast<u32x2*>(head + (row0 + R * grp + r) * kDim + 4 * lane8 + 32 * c));
+                    u32x4{pack_bf16(v.x, v.y), pack_bf16(v.z, v.w), pack_bf16(u.x, u.y),
+                          pack_bf16(u.z, u.w)},
+                    reinterpret_cast<u32x4*>(head + (row0 + R * grp + r) * kDim +
+                                             tcol<uint16_t>(lane8, 2 * m)));
             }
     }
 };
@@ -119,13 +136,13 @@ template <int R> struct TileIO<uint16_t, R> {
 // 2m+1's in lanes 4-7 (hi), identical in the four lanes of a half: five
 // instructions a pair where a sum in all eight lanes would take six, and the
 // per-row arithmetic that follows is done by half as many lanes per row.
-template <int R>
+template <typename StateT, int R>
 __device__ __forceinline__ void tile_dot_split(const f32x4 (&h)[R][4], const float* x, int lane8, bool hi,
                                                float (&out)[R / 2])
 {
     f32x4 xv[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) xv[c] = ld4(x + 4 * lane8 + 32 * c);
+    for (int c = 0; c < 4; ++c) xv[c] = ld4(x + tcol<StateT>(lane8, c));
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -527,7 +544,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         if (pp >= P) break;
         const float g0 = L.g0[pp];
         float pk[RH];
-        tile_dot_split<R>(h, (CH && SNAP ? L.kx : L.khat) + pp * kDim, lane8, hi, pk);
+        tile_dot_split<StateT, R>(h, (CH && SNAP ? L.kx : L.khat) + pp * kDim, lane8, hi, pk);
         float u[RH];
 #pragma unroll
         for (int m = 0; m < RH; ++m) u[m] = g0 * pk[m];
@@ -544,7 +561,7 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
         for (int m = 0; m < RH; ++m) L.dw[pp * kRowsPerWg + rm + 2 * m] = dreg[pp][m];  // same value in 4 lanes
 
         float pq[RH];
-        tile_dot_split<R>(h, (CH && SNAP ? L.qx : L.qt) + pp * kDim, lane8, hi, pq);
+        tile_dot_split<StateT, R>(h, (CH && SNAP ? L.qx : L.qt) + pp * kDim, lane8, hi, pq);
         float o[RH];
 #pragma unroll
         for (int m = 0; m < RH; ++m) o[m] = g0 * pq[m];
@@ -587,8 +604,8 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
             f32x4 kh[4], dc[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                kh[c] = ld4(L.khat + t * kDim + 4 * lane8 + 32 * c);
-                dc[c] = CH ? ld4(L.al + t * kDim + 4 * lane8 + 32 * c) : f32x4{g, g, g, g};
+                kh[c] = ld4(L.khat + t * kDim + tcol<StateT>(lane8, c));
+                dc[c] = CH ? ld4(L.al + t * kDim + tcol<StateT>(lane8, c)) : f32x4{g, g, g, g};
             }
             float dr[R];              // both rows of each pair, from the two halves
 #pragma unroll
