@@ -26,16 +26,23 @@
 // memory floor, but matrix-core versions measured slower (fp32 16x16x4 with half
 // of the columns idle at w = 4; 4x4x1 with none idle): the products then make a
 // round trip through LDS to a per-row recurrence, which costs more than the
-// vector fmas it saves. So the contraction stays on the vector ALU, fused with
-// the recurrence in registers.
+// vector fmas it saves. On bf16 pools a 16x16x32 bf16 version (the window
+// vectors split exactly into three bf16 parts) halves the vector instructions,
+// but the matrix layout wants sixteen rows across neighbouring lanes where the
+// coalesced loads put one row: moving the tile between the two layouts with
+// lane permutes costs as much LDS time as the fmas save, and loading it in the
+// matrix layout halves the row segments each load covers. So the contraction
+// stays on the vector ALU, fused with the recurrence in registers.
 //
 // One workgroup per (row, value head, chunk of NT/8*R head rows): eight wave64s
 // covering the whole head for windows of up to 4 positions, four wave64s per
 // half head for longer ones;
 // workgroup ids are remapped so that each XCD streams a contiguous stretch of
-// the pool. Thread t holds head rows row0 + R*(t/8) + r and columns
-// 4*(t%8) + 32*c + e (c, e = 0..3): each 16-byte load of eight neighbouring
-// lanes covers a whole 128-byte row segment, and a length-128 reduction is 16
+// the pool. Thread t holds head rows row0 + R*(t/8) + r and 16 of their
+// columns, 4*(t%8) + 32*c + e (c, e = 0..3) on fp32 pools and 8*(t%8) + 64*m + e
+// (m = 0..1, e = 0..7) on bf16 pools: either way each 16-byte load of eight
+// neighbouring lanes covers a whole 128-byte row segment, and a length-128
+// reduction is 16
 // fmas in the lane plus three DPP steps over the eight lanes of a row group,
 // arranged so that lanes 0-3 end with the even rows' sums and lanes 4-7 with
 // the odd rows' (the per-row recurrence then runs in four lanes per row, not
