@@ -558,7 +558,9 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
     const int64_t conv_layer = conv ? (int64_t)p.num_rows * p.conv.wgs_per_row : 0;
     // layers per launch: all of them unless the grid would pass the
     // dispatch limit (the host entry point has checked that one layer fits)
+    if (ssm_layer + conv_layer == 0) return hipSuccess;
     const int64_t per = (kMaxLaunchWgs - kNumXcd) / (ssm_layer + conv_layer);
+    if (per < 1) return hipErrorInvalidConfiguration;
     const int step = per >= p.num_layers ? p.num_layers : (int)per;
     for (int l0 = 0; l0 < p.num_layers; l0 += step) {
         CommitParams args = p;
