@@ -34,15 +34,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 
-// Round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// Two values rounded to bf16, nearest with ties to even, packed (lo in the
+// low half): gfx950's conversion instruction, one per pair. It rounds fp32
+// subnormals too (they are kept: no flush-to-zero here) and gives a quiet NaN
+// for a NaN; a GPU test holds it to an integer round-to-nearest-even over the
+// whole fp32 range.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---- DPP lane exchange -----------------------------------------------------

@@ -207,3 +207,53 @@ def test_commit_beyond_one_launch(gdn, dtype, rows):
         idx = torch.as_tensor(keep, device="cuda")
         assert torch.equal(pool_bits(state[layer].index_select(0, idx)),
                            pool_bits(pre[layer].index_select(0, idx))), f"layer {layer}"
+
+
+def test_bf16_commit_rounding_across_the_fp32_range(gdn):
+    """The bf16 commit rounds each final state value once, to nearest even
+    (vLLM RecoverSSM PR, Test Plan: bf16 state). Records seeded directly: a
+    zero checkpoint, decay 1, corrections with random full 24-bit mantissas,
+    and keys that are signed powers of two from 2^-134 to 2^120, so the
+    committed value fma(delta[v], key[k], 0) is delta[v] scaled exactly (or
+    rounded once into the fp32 subnormal range) across the whole fp32 range:
+    fp32 subnormals, bf16 ties of both parities, values that round up into the
+    next binade or overflow to infinity, infinite corrections. Every stored bf16
+    value equals the oracle's integer RNE of the oracle's replay bit for bit
+    (NaN corrections: a NaN, whose payload IEEE leaves open)."""
+    rng = np.random.default_rng(151)
+    rows, HV, T = 4, 8, 1
+    H = rows * HV
+    m = rng.integers(0, 1 << 23, size=(H, 128), dtype=np.uint32)
+    e = rng.integers(127 - 12, 127 + 12, size=(H, 128), dtype=np.uint32)
+    s = rng.integers(0, 2, size=(H, 128), dtype=np.uint32)
+    m[:, :16] = (m[:, :16] & ~np.uint32(0xffff)) | np.uint32(0x8000)        # exact ties
+    m[:, 16:24] = (m[:, 16:24] & ~np.uint32(0xffff)) | np.uint32(0x7fff)    # just below
+    m[:, 24:32] = (m[:, 24:32] & ~np.uint32(0xffff)) | np.uint32(0x8001)    # just above
+    m[:, 32:36] = np.uint32(0x7fffff)                                       # round to next binade
+    delta = ((s << 31) | (e << 23) | m).view(np.float32).copy()
+    delta[0, 40] = np.inf
+    delta[1, 41] = -np.inf
+    delta[2, 42] = np.nan
+    kexp = -134 + 2 * np.arange(128)                                       # 2^-134 .. 2^120
+    keys = np.ldexp(np.where(np.arange(128) % 3 == 0, -1.0, 1.0), kexp).astype(np.float32)
+    keys = np.broadcast_to(keys, (H, 128)).copy()
+    state = torch.zeros((1, rows, HV, 128, 128), dtype=torch.bfloat16, device="cuda")
+    rec = G.Pools.alloc_records(1, rows, HV, T)
+    rec[0, :, :, :128] = torch.as_tensor(delta.reshape(rows, HV, 128), device="cuda")
+    rec[0, :, :, 128:256] = torch.as_tensor(keys.reshape(rows, HV, 128), device="cuda")
+    rec[0, :, :, 256] = 1.0
+    pools = G.Pools(state, rec, HV, T)
+    slots = dev_i32(np.arange(rows))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    G.gdn_commit_all_layers(pools, slots, slots, slots, dev_i32(np.ones(rows)), err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want = oracle.replay_heads(np.zeros((H, 128, 128), np.float32), np.ones(H, np.int32),
+                               delta[:, None, :], keys[:, None, :], np.ones((H, 1), np.float32))
+    assert np.isinf(want).any() and (np.abs(want[np.isfinite(want)]) < 2.0 ** -126).any()
+    want_bits = oracle.f32_to_bf16_rne(want)
+    got_bits = state.view(torch.int16).cpu().numpy().view(np.uint16).reshape(H, 128, 128)
+    nan = np.isnan(want)
+    assert np.array_equal(got_bits[~nan], want_bits[~nan]), int((got_bits != want_bits)[~nan].sum())
+    got_nan = ((got_bits & 0x7f80) == 0x7f80) & ((got_bits & 0x7f) != 0)
+    assert got_nan[nan].all()
