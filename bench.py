@@ -47,8 +47,10 @@ CHANNEL_GATE_BYTES = 128 * 4 + 4                 # per-channel log-decays and be
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 _CSRC = "gated_deltanet_speculative_gdn_amd/csrc/"
 KERNEL_SOURCES = {
-    "commit_all_layers": [_CSRC + "gdn_commit.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp"],
-    "verify": [_CSRC + "gdn_verify.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp"],
+    "commit_all_layers": [_CSRC + "gdn_commit.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp",
+                          _CSRC + "gdn_divide.hpp"],
+    "verify": [_CSRC + "gdn_verify.hip", _CSRC + "gdn_device.hpp", _CSRC + "gdn_kernels.hpp",
+               _CSRC + "gdn_divide.hpp"],
 }
 
 

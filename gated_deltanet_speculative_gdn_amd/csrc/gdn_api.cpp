@@ -188,6 +188,7 @@ int32_t gdn_verify(const gdn_pools* pools, int32_t layer, int32_t num_rows,
     v.num_slots = pools->num_state_slots;
     v.num_rec_slots = pools->num_rec_slots;
     v.T = pools->rec_tokens;
+    v.div_hv = make_divider((uint32_t)v.hv);
     return launched(launch_verify(v, pools->state_dtype == GDN_STATE_BF16, (hipStream_t)stream));
 }
 
@@ -225,6 +226,7 @@ int32_t gdn_native_window(const gdn_pools* pools, int32_t layer, int32_t num_row
     v.num_slots = pools->num_state_slots;
     v.num_rec_slots = pools->num_rec_slots;
     v.T = pools->rec_tokens;
+    v.div_hv = make_divider((uint32_t)v.hv);
     return launched(
         launch_native_window(v, pools->state_dtype == GDN_STATE_BF16, (hipStream_t)stream));
 }
@@ -304,8 +306,11 @@ int32_t gdn_commit_all_layers_conv(const gdn_pools* pools, const gdn_conv_pools*
         v.num_slots = conv->num_slots;
         v.pieces = (int32_t)(v.row_bytes / 16);
         v.wgs_per_row = (int32_t)conv_per_row;
+        v.div_wpr = make_divider((uint32_t)conv_per_row);
         c.conv_wgs = (int64_t)num_rows * layers * conv_per_row;
     }
+    c.div_hv = make_divider((uint32_t)c.hv);
+    c.div_rows = make_divider((uint32_t)num_rows);
     const bool bf16 = pools && pools->state_dtype == GDN_STATE_BF16;
     return launched(launch_commit(c, bf16, bnd_len != nullptr, (hipStream_t)stream));
 }
@@ -352,6 +357,8 @@ int32_t gdn_native_accept(const gdn_pools* pools, void* const* snap_layers, int3
     a.hv = pools->num_v_heads;
     a.num_slots = pools->num_state_slots;
     a.T = pools->rec_tokens;
+    a.div_hv = make_divider((uint32_t)a.hv);
+    a.div_rows = make_divider((uint32_t)num_rows);
     return launched(
         launch_native_accept(a, pools->state_dtype == GDN_STATE_BF16, (hipStream_t)stream));
 }

@@ -142,10 +142,10 @@ __device__ void conv_compact(const CommitParams& p, int64_t id)
 {
     static_assert(kConvPiecesPerWg == kThreads, "one piece per thread");
     const ConvParams& c = p.conv;
-    const int chunk = (int)(id % c.wgs_per_row);
-    const int64_t lb = id / c.wgs_per_row;
-    const int b = (int)(lb % p.num_rows);
-    const int layer = (int)(lb / p.num_rows);
+    const uint32_t lb = udiv((uint32_t)id, c.div_wpr);
+    const int chunk = (int)((uint32_t)id - lb * (uint32_t)c.wgs_per_row);
+    const int layer = (int)udiv(lb, p.div_rows);
+    const int b = (int)(lb - (uint32_t)layer * (uint32_t)p.num_rows);
     const int n = p.n[b];
     if (n == 0) return;
     const int src = p.src[b];
@@ -219,14 +219,14 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
                                       // per-channel records: [n][128] decays)
 
     // logical id: (layer, row, value head, part), XCD-contiguous
-    const int64_t wr = (int64_t)blockIdx.x - conv_off;
-    const int64_t wg = kCommitXcdRemap ? xcd_contiguous_id(wr, p.ssm_wgs) : wr;
+    const uint32_t wr = blockIdx.x - (uint32_t)conv_off;
+    const uint32_t wg = kCommitXcdRemap ? xcd_contiguous_id(wr, (uint32_t)p.ssm_wgs) : wr;
     const int part = (int)(wg % SPLIT);
-    const int64_t head_id = wg / SPLIT;
-    const int hv = (int)(head_id % p.hv);
-    const int64_t lb = head_id / p.hv;
-    const int b = (int)(lb % p.num_rows);
-    const int layer = (int)(lb / p.num_rows);
+    const uint32_t head_id = wg / SPLIT;
+    const uint32_t lb = udiv(head_id, p.div_hv);
+    const int hv = (int)(head_id - lb * (uint32_t)p.hv);
+    const int layer = (int)udiv(lb, p.div_rows);
+    const int b = (int)(lb - (uint32_t)layer * (uint32_t)p.num_rows);
 
     // ---- row decode ----
     const int n = p.n[b];
@@ -513,11 +513,11 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(CommitParams p)
 template <typename StateT>
 __global__ void __launch_bounds__(kThreads) accept_kernel(AcceptParams p)
 {
-    const int64_t wg = blockIdx.x;
-    const int hv = (int)(wg % p.hv);
-    const int64_t lb = wg / p.hv;
-    const int b = (int)(lb % p.num_rows);
-    const int layer = (int)(lb / p.num_rows);
+    const uint32_t wg = blockIdx.x;
+    const uint32_t lb = udiv(wg, p.div_hv);
+    const int hv = (int)(wg - lb * (uint32_t)p.hv);
+    const int layer = (int)udiv(lb, p.div_rows);
+    const int b = (int)(lb - (uint32_t)layer * (uint32_t)p.num_rows);
     const int n = p.n[b];
     if (n == 0) return;
     const int dst = p.dst[b];

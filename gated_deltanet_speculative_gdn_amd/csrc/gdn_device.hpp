@@ -118,8 +118,8 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* base, int idx) {
 // memory instead of every eighth piece. A bijection on [0, grid); the tail
 // past the last multiple of 8 keeps its id.
 constexpr int kNumXcd = 8;
-__device__ __forceinline__ int64_t xcd_contiguous_id(int64_t w, int64_t grid) {
-    const int64_t per = grid / kNumXcd;
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t w, uint32_t grid) {
+    const uint32_t per = grid / kNumXcd;
     return w < per * kNumXcd ? (w % kNumXcd) * per + w / kNumXcd : w;
 }
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_divide.hpp"
 #include "gdn_replay.h"
 
 namespace gdn {
@@ -30,6 +31,7 @@ struct VerifyParams {
     int64_t rec_stride;       // floats per (record slot, value head)
     int32_t* err;
     int32_t num_rows, hv, group, num_slots, num_rec_slots, T;
+    Divider div_hv;           // division by hv
     float scale;
     bool raw_gates;           // gates from raw a, b with A_log, dt_bias
     bool out_bf16;            // outputs rounded to bf16 (nearest even)
@@ -51,6 +53,7 @@ struct ConvParams {
     int32_t state_len, num_slots;
     int32_t pieces;                     // 16-byte pieces per row
     int32_t wgs_per_row;                // workgroups per (layer, row)
+    Divider div_wpr;                    // division by wgs_per_row
 };
 
 // The all-layer commit.
@@ -66,6 +69,7 @@ struct CommitParams {
     int32_t* err;
     int64_t rec_stride;
     int32_t num_layers, num_rows, hv, num_slots, num_rec_slots, T;
+    Divider div_hv, div_rows; // division by hv and num_rows
     bool payload;             // payload records: the replay recomputes the corrections
     bool channel;             // per-channel decay records: alpha[T][K] in place of the gate
     int64_t ssm_wgs;          // workgroups of the state replay (after the conv's, below)
@@ -82,6 +86,7 @@ struct AcceptParams {
     const int32_t* n;
     int32_t* err;
     int32_t num_layers, num_rows, hv, num_slots, T;
+    Divider div_hv, div_rows;
 };
 
 struct PlanParams {

@@ -215,11 +215,11 @@ __global__ void __launch_bounds__(NT) verify_kernel(VerifyParams p)
     const int T = p.T;   // record capacity (record addressing); T <= TT
     const Lds<TT, kRowsPerWg, CH, SNAP> L(lds_raw);
 
-    const int64_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const uint32_t item = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int chunk = (int)(item % kChunks);
-    const int64_t bh = item / kChunks;
-    const int b = (int)(bh / p.hv);
-    const int hv = (int)(bh - (int64_t)b * p.hv);
+    const uint32_t bh = item / kChunks;
+    const int b = (int)udiv(bh, p.div_hv);
+    const int hv = (int)(bh - (uint32_t)b * (uint32_t)p.hv);
     const int row0 = chunk * kRowsPerWg;
     const bool lead = chunk == 0;
 
