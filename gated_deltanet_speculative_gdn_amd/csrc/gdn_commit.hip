@@ -26,9 +26,9 @@
 // the boundary state kept in a second register tile. State loads and stores
 // are nontemporal (streamed past the caches: nothing here is reused), and the
 // workgroup ids are remapped so that each XCD streams a contiguous range of
-// heads. Launches for windows of up to four records are held to six
-// workgroups per CU through their LDS request (fewer bytes in flight per CU
-// stream faster). Because every thread reads all of
+// heads. Launches are held to six workgroups per CU through their LDS
+// request (fewer bytes in flight per CU stream faster), except align-mode
+// launches over more than eight records. Because every thread reads all of
 // its source elements before its first store and writes only the elements it
 // read, a destination or boundary slot equal to the source slot is safe; the
 // pages' read-after-overwrite race between programs cannot occur.
@@ -543,19 +543,19 @@ __global__ void __launch_bounds__(kThreads) accept_kernel(AcceptParams p)
     for (int i = 0; i < kPer; ++i) __builtin_nontemporal_store(x[i], o4 + threadIdx.x + kThreads * i);
 }
 
-// LDS requested per workgroup. A launch whose record capacity is at most
-// kShortRecTokens asks for at least kShortLdsFloor bytes, which holds it to six
-// workgroups per CU (of 160 KiB) where the waves alone would allow eight:
-// 48 KiB of state in flight per CU instead of 64. HBM streams this access
-// pattern faster with fewer bytes queued per CU; longer rings (more records
-// staged per workgroup, align-mode second stores) stream best at full
-// occupancy.
-constexpr int kShortRecTokens = 4;
-constexpr size_t kShortLdsFloor = 24 * 1024;
-size_t commit_lds_request(int T, bool channel)
+// LDS requested per workgroup. A launch asks for at least kLdsFloor bytes,
+// which holds it to six workgroups per CU (of 160 KiB) where the waves alone
+// would allow eight: 48 KiB of state in flight per CU instead of 64, which HBM
+// streams faster. The exception is an align-mode launch with more than
+// kAlignFloorRecTokens records: with its long record staging and the second
+// (boundary) store it streams as well or better at full occupancy.
+constexpr int kAlignFloorRecTokens = 8;
+constexpr size_t kLdsFloor = 24 * 1024;
+size_t commit_lds_request(int T, bool channel, bool align)
 {
     const size_t need = commit_lds_bytes(T, channel);
-    return T <= kShortRecTokens && need < kShortLdsFloor ? kShortLdsFloor : need;
+    const bool capped = !align || T <= kAlignFloorRecTokens;
+    return capped && need < kLdsFloor ? kLdsFloor : need;
 }
 
 template <typename StateT, bool ALIGN, int SPLIT>
@@ -595,7 +595,7 @@ hipError_t launch_c(const CommitParams& p, hipStream_t s)
         const uint64_t grid = (uint64_t)(args.ssm_wgs + conv_off);
         void* kargs[] = {&args};
         const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs,
-                                             commit_lds_request(p.T, p.channel), s);
+                                             commit_lds_request(p.T, p.channel, ALIGN), s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
